@@ -1,0 +1,81 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and its host-only functions (layout, sizes, shape checks, error
+strings) agree with the oracle and the closed forms.  No device calls."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from transformer_lm_pretraining_gpt2_amd import binding
+from transformer_lm_pretraining_gpt2_amd.config import CONFIGS, GPT2Config, num_params
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "gpt2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gpt2_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = binding.lib()
+    names = header_functions()
+    assert len(names) >= 19
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(n for n, _, _ in binding.SIGNATURES) == names
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_layout_matches_oracle_and_closed_form(oracle, name):
+    m = CONFIGS[name].model
+    assert binding.num_params(m) == num_params(m) == oracle.num_params(m)
+    lay = binding.param_layout(m)
+    assert lay == oracle.param_layout(m)
+    n_decay = sum(e["rows"] * e["cols"] for e in lay if e["decay"])
+    assert binding.num_decay_params(m) == n_decay
+
+
+def test_workspace_and_shape_checks():
+    m = CONFIGS["gpt2_124m"].model
+    ws = binding.workspace_bytes(m, 16, 1024, binding.GPT2_BF16)
+    assert 4e9 < ws < 20e9
+    assert binding.workspace_bytes(m, 16, 1024, binding.GPT2_FP32) > ws
+    assert binding.check_shapes(m, 16, 1024) == 0
+    assert binding.check_shapes(m, 16, 1000) == -2  # T % 64
+    assert binding.check_shapes(m, 16, 2048) == -2  # T > max_seq_len
+    assert binding.check_shapes(m, 1, 64) == -2  # B*T % 128
+    bad = [GPT2Config(50257, 50257, 12, 12, 768, 1024),  # Vp % 128
+           GPT2Config(50257, 50176, 12, 12, 768, 1024),  # Vp < V
+           GPT2Config(512, 512, 2, 3, 128, 64),  # C % nh
+           GPT2Config(512, 512, 2, 1, 128, 64),  # head_dim 128
+           GPT2Config(512, 512, 2, 2, 96, 64)]  # C % 128
+    for c in bad:
+        assert binding.num_params(c) == -1
+        assert binding.check_shapes(c, 4, 64) == -1
+
+
+def test_init_rejects_bad_arguments_without_touching_the_device():
+    m = CONFIGS["tiny"].model
+    c = binding.cconfig(m)
+    h = ctypes.c_void_p()
+    L = binding.lib()
+    ws = binding.workspace_bytes(m, 4, 64, 0)
+    fake = 1 << 20  # 256-aligned address; argument checks fail before any device call
+    assert L.gpt2_init(ctypes.byref(h), ctypes.byref(c), 0, 4, 64, fake + 4, None, fake, fake, fake, fake, ws, None) == -3
+    assert L.gpt2_init(ctypes.byref(h), ctypes.byref(c), 0, 4, 64, fake, None, fake, fake, fake, fake, ws - 1, None) == -7
+    assert L.gpt2_init(ctypes.byref(h), ctypes.byref(c), 1, 4, 64, fake, None, fake, fake, fake, fake, ws, None) == -3
+    assert L.gpt2_init(ctypes.byref(h), ctypes.byref(c), 0, 4, 96, fake, None, fake, fake, fake, fake, ws, None) == -2
+    assert L.gpt2_backward(None, 0, 1) == -3
+
+
+def test_error_strings_and_kernel_names():
+    L = binding.lib()
+    for code in binding.ERRORS:
+        assert L.gpt2_strerror(code)
+    names = binding.kernel_names()
+    assert "gemm_nt_store" in names and "attn_fwd" in names and "adamw" in names
+    assert L.gpt2_kernel_name(len(names)) is None

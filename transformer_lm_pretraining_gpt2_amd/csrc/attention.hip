@@ -1,0 +1,481 @@
+// attention.hip -- causal multi-head self-attention on MFMA for gfx950.
+//
+// Per head: y_i = sum_{j<=i} softmax_j(q_i . k_j / sqrt(hd)) v_j, computed
+// tile by tile with an online softmax so the T x T score matrix never leaves
+// registers ("Karpathy's four-hour GPT-2 reproduction in one post", part 2:
+// Flash Attention; "Reproducing GPT-2 (124M) cheaply with llm.c", setup:
+// FlashAttention).  The forward pass saves the per-row log-sum-exp; the
+// backward pass recomputes probabilities from it.
+//
+// Layout: qkv is [B*T, 3C] with q heads, then k heads, then v heads
+// (head h at column offset h*hd inside each third); out / dout are [B*T, C].
+// Each wave owns 32 query (or key) rows; a block of 4 waves shares K/V (or
+// Q/dO) tiles of 64 rows through LDS.
+//
+// Orientation: scores are produced as S^T (keys x queries) in the forward and
+// dQ kernels, so every lane owns one query column and its softmax statistics
+// (max, sum, LSE, D) are per-lane scalars shared with the partner lane l^32.
+// The dK/dV kernel produces S (queries x keys) so each lane owns one key.
+// The second product of each pair consumes the accumulator directly as its
+// k-operand: the 16 reduction slots of a (virtual) 32x32x16 MFMA may be any
+// 16 keys as long as both operands use the same assignment, here
+// key(c, g, s) = 16c + 8(s/4) + 4g + s%4 for chunk c, lane group g, slot s.
+#include "common.h"
+#include "kernels.h"
+
+namespace gpt2k {
+namespace {
+
+constexpr int KT = 64;   // rows per K/V (or Q/dO) LDS tile
+constexpr int WQ = 32;   // rows per wave
+constexpr int NW = 4;    // waves per block
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+template <typename T> struct V16;
+template <> struct V16<bf16> { typedef bf16x8 type; static constexpr int n = 8; };
+template <> struct V16<float> { typedef f32x4 type; static constexpr int n = 4; };
+
+// Copy a [KT][HD] row tile (rows `ld` apart in global) into LDS [KT][HD+pad].
+template <typename T, int HD>
+__device__ __forceinline__ void load_rows(T* s, const T* g, int64_t ld, int tid) {
+  constexpr int VE = V16<T>::n, LD = HD + VE, CPR = HD / VE, TOTAL = KT * CPR;
+  for (int idx = tid; idx < TOTAL; idx += NW * 64) {
+    const int r = idx / CPR, c = idx % CPR;
+    *reinterpret_cast<f32x4*>(s + r * LD + c * VE) = *reinterpret_cast<const f32x4*>(g + (int64_t)r * ld + c * VE);
+  }
+}
+
+// Copy a [KT][HD] row tile into LDS transposed: [HD][KT+pad].
+template <typename T, int HD>
+__device__ __forceinline__ void load_rows_t(T* s, const T* g, int64_t ld, int tid) {
+  typedef typename V16<T>::type V;
+  typedef typename Frag<T>::type F;
+  constexpr int VE = V16<T>::n, LD = KT + VE, NCB = HD / VE, TOTAL = (KT / 8) * NCB;
+  for (int blk = tid; blk < TOTAL; blk += NW * 64) {
+    const int rb = blk / NCB, cb = blk % NCB;
+    V v[8];
+#pragma unroll
+    for (int a = 0; a < 8; a++) v[a] = *reinterpret_cast<const V*>(g + (int64_t)(rb * 8 + a) * ld + cb * VE);
+#pragma unroll
+    for (int b = 0; b < VE; b++) {
+      F w;
+#pragma unroll
+      for (int a = 0; a < 8; a++) w[a] = v[a][b];
+      st8(s + (cb * VE + b) * LD + rb * 8, w);
+    }
+  }
+}
+
+// k-operand fragment from a transposed tile [rows][KT+pad]: row `row`, chunk c,
+// lane group g -> columns 16c+4g .. +3 and 16c+8+4g .. +3.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type ld_split(const T* s, int ldr, int row, int c, int g) {
+  typedef typename Quad<T>::type Q;
+  const Q lo = *reinterpret_cast<const Q*>(s + row * ldr + 16 * c + 4 * g);
+  const Q hi = *reinterpret_cast<const Q*>(s + row * ldr + 16 * c + 8 + 4 * g);
+  typename Frag<T>::type f;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    f[e] = lo[e];
+    f[4 + e] = hi[e];
+  }
+  return f;
+}
+
+// Slots 8h..8h+7 of a 32x32 accumulator as a k-operand fragment.
+template <typename T>
+__device__ __forceinline__ typename Frag<T>::type acc_frag(const f32x16& a, int h) {
+  typename Frag<T>::type f;
+#pragma unroll
+  for (int e = 0; e < 8; e++) f[e] = from_f<T>(a[8 * h + e]);
+  return f;
+}
+
+// ------------------------------------------------------------------------
+// Forward.  grid (ceil(T/128), NH, B); heavy (late) query blocks first.
+// ------------------------------------------------------------------------
+template <typename T, int HD>
+__global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ out,
+                                                           float* __restrict__ lse, int T_, int NH, float sl2) {
+  constexpr int VE = V16<T>::n, LDK = HD + VE, LDV = KT + VE, ND = HD / 16, NDT = HD / 32;
+  typedef typename Frag<T>::type F;
+  typedef typename Quad<T>::type Q;
+  __shared__ __attribute__((aligned(16))) T Ks[KT * LDK];
+  __shared__ __attribute__((aligned(16))) T Vt[HD * LDV];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  const int qblk = gridDim.x - 1 - blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int C = NH * HD, S3 = 3 * C;
+  const int q0 = qblk * NW * WQ + w * WQ;
+  const bool active = q0 < T_;
+  const T* base = qkv + (int64_t)b * T_ * S3;
+
+  F qf[ND];
+  if (active) {
+#pragma unroll
+    for (int ds = 0; ds < ND; ds++) qf[ds] = ld8(base + (int64_t)(q0 + lr) * S3 + h * HD + ds * 16 + 8 * lg);
+  }
+  f32x16 o[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; dt++) o[dt] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+  const int q = q0 + lr;
+
+  const int kv_end = min(T_, (qblk + 1) * NW * WQ);
+  for (int kv0 = 0; kv0 < kv_end; kv0 += KT) {
+    __syncthreads();
+    load_rows<T, HD>(Ks, base + (int64_t)kv0 * S3 + C + h * HD, S3, tid);
+    load_rows_t<T, HD>(Vt, base + (int64_t)kv0 * S3 + 2 * C + h * HD, S3, tid);
+    __syncthreads();
+    if (!active || kv0 > q0 + WQ - 1) continue;
+    f32x16 s[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; c2++) {
+      s[c2] = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < ND; ds++) mma16(s[c2], ld8(Ks + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), qf[ds]);
+    }
+    // scale into the log2 domain, mask keys after the query
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; c2++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int kv = kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+        const float t = kv <= q ? s[c2][r] * sl2 : -INFINITY;
+        s[c2][r] = t;
+        mx = fmaxf(mx, t);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);
+    const float alpha = exp2f(m - mn);
+    float rs = 0.f;
+#pragma unroll
+    for (int c2 = 0; c2 < 2; c2++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float p = exp2f(s[c2][r] - mn);
+        s[c2][r] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 32, 64);
+    l = l * alpha + rs;
+    m = mn;
+#pragma unroll
+    for (int dt = 0; dt < NDT; dt++) o[dt] *= alpha;
+#pragma unroll
+    for (int c = 0; c < KT / 16; c++) {
+      const F pf = acc_frag<T>(s[c / 2], c % 2);
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++) mma16(o[dt], ld_split(Vt, LDV, dt * 32 + lr, c, lg), pf);
+    }
+  }
+  if (!active) return;
+  const float inv = 1.f / l;
+  T* orow = out + ((int64_t)b * T_ + q) * C + h * HD;
+#pragma unroll
+  for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+    for (int qq = 0; qq < 4; qq++) {
+      Q v;
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[e] = from_f<T>(o[dt][4 * qq + e] * inv);
+      *reinterpret_cast<Q*>(orow + dt * 32 + 8 * qq + 4 * lg) = v;
+    }
+  if (lg == 0) lse[((int64_t)b * NH + h) * T_ + q] = (m + log2f(l)) * LN2;
+}
+
+// ------------------------------------------------------------------------
+// D[b,h,i] = sum_d dout[i, h*hd + d] * out[i, h*hd + d]
+// ------------------------------------------------------------------------
+template <typename T, int HD>
+__global__ void attn_dsum_kernel(const T* __restrict__ out, const T* __restrict__ dout, float* __restrict__ dsum, int T_,
+                                 int NH, int64_t n) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n) return;
+  const int h = idx % NH;
+  const int64_t row = idx / NH;  // b*T + t
+  const int C = NH * HD;
+  const T* o = out + row * C + h * HD;
+  const T* d = dout + row * C + h * HD;
+  float s = 0.f;
+#pragma unroll 2
+  for (int k = 0; k < HD; k += 8) {
+    const auto a = ld8(o + k);
+    const auto c = ld8(d + k);
+#pragma unroll
+    for (int e = 0; e < 8; e++) s += to_f<T>(a[e]) * to_f<T>(c[e]);
+  }
+  const int64_t b = row / T_, t = row % T_;
+  dsum[(b * NH + h) * T_ + t] = s;
+}
+
+// ------------------------------------------------------------------------
+// dQ.  grid (ceil(T/128), NH, B).  Per query column (one per lane):
+// P^T = exp(S^T - LSE), dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ = scale dS K.
+// ------------------------------------------------------------------------
+template <typename T, int HD>
+__global__ void __launch_bounds__(NW * 64) attn_dq_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
+                                                          const float* __restrict__ lse, const float* __restrict__ dsum,
+                                                          T* __restrict__ dqkv, int T_, int NH, float sl2, float scale) {
+  constexpr int VE = V16<T>::n, LDK = HD + VE, LDV = KT + VE, ND = HD / 16, NDT = HD / 32;
+  typedef typename Frag<T>::type F;
+  typedef typename Quad<T>::type Q;
+  __shared__ __attribute__((aligned(16))) T Ks[KT * LDK];
+  __shared__ __attribute__((aligned(16))) T Vs[KT * LDK];
+  __shared__ __attribute__((aligned(16))) T Kt[HD * LDV];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  const int qblk = gridDim.x - 1 - blockIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int C = NH * HD, S3 = 3 * C;
+  const int q0 = qblk * NW * WQ + w * WQ;
+  const bool active = q0 < T_;
+  const T* base = qkv + (int64_t)b * T_ * S3;
+  const int q = q0 + lr;
+
+  F qf[ND], df[ND];
+  float lse2 = 0.f, dq_d = 0.f;
+  if (active) {
+#pragma unroll
+    for (int ds = 0; ds < ND; ds++) {
+      qf[ds] = ld8(base + (int64_t)q * S3 + h * HD + ds * 16 + 8 * lg);
+      df[ds] = ld8(dout + ((int64_t)b * T_ + q) * C + h * HD + ds * 16 + 8 * lg);
+    }
+    lse2 = lse[((int64_t)b * NH + h) * T_ + q] * LOG2E;
+    dq_d = dsum[((int64_t)b * NH + h) * T_ + q];
+  }
+  f32x16 dq[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; dt++) dq[dt] = f32x16{};
+
+  const int kv_end = min(T_, (qblk + 1) * NW * WQ);
+  for (int kv0 = 0; kv0 < kv_end; kv0 += KT) {
+    __syncthreads();
+    load_rows<T, HD>(Ks, base + (int64_t)kv0 * S3 + C + h * HD, S3, tid);
+    load_rows<T, HD>(Vs, base + (int64_t)kv0 * S3 + 2 * C + h * HD, S3, tid);
+    load_rows_t<T, HD>(Kt, base + (int64_t)kv0 * S3 + C + h * HD, S3, tid);
+    __syncthreads();
+    if (!active || kv0 > q0 + WQ - 1) continue;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; c2++) {
+      s[c2] = f32x16{};
+      dp[c2] = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < ND; ds++) {
+        mma16(s[c2], ld8(Ks + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), qf[ds]);
+        mma16(dp[c2], ld8(Vs + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), df[ds]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int kv = kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+        const float p = kv <= q ? exp2f(s[c2][r] * sl2 - lse2) : 0.f;
+        s[c2][r] = p * (dp[c2][r] - dq_d);  // dS^T
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < KT / 16; c++) {
+      const F sf = acc_frag<T>(s[c / 2], c % 2);
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++) mma16(dq[dt], ld_split(Kt, LDV, dt * 32 + lr, c, lg), sf);
+    }
+  }
+  if (!active) return;
+  T* row = dqkv + ((int64_t)b * T_ + q) * S3 + h * HD;
+#pragma unroll
+  for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+    for (int qq = 0; qq < 4; qq++) {
+      Q v;
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[e] = from_f<T>(dq[dt][4 * qq + e] * scale);
+      *reinterpret_cast<Q*>(row + dt * 32 + 8 * qq + 4 * lg) = v;
+    }
+}
+
+// ------------------------------------------------------------------------
+// dK, dV.  grid (ceil(T/128), NH, B); each wave owns 32 keys and walks the
+// query tiles at or after them.  Per key column (one per lane):
+// P = exp(S - LSE), dV += dO^T P, dP = dO V^T, dS = P (dP - D), dK += scale Q^T dS.
+// ------------------------------------------------------------------------
+template <typename T, int HD>
+__global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
+                                                           const float* __restrict__ lse, const float* __restrict__ dsum,
+                                                           T* __restrict__ dqkv, int T_, int NH, float sl2, float scale) {
+  constexpr int VE = V16<T>::n, LDK = HD + VE, LDV = KT + VE, ND = HD / 16, NDT = HD / 32;
+  typedef typename Frag<T>::type F;
+  typedef typename Quad<T>::type Q;
+  __shared__ __attribute__((aligned(16))) T Qs[KT * LDK];
+  __shared__ __attribute__((aligned(16))) T Ds[KT * LDK];
+  __shared__ __attribute__((aligned(16))) T Qt[HD * LDV];
+  __shared__ __attribute__((aligned(16))) T Dt[HD * LDV];
+  __shared__ float Ls[KT], Dd[KT];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  const int kblk = blockIdx.x;  // early key blocks see the most queries: they go first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int C = NH * HD, S3 = 3 * C;
+  const int k0 = kblk * NW * WQ + w * WQ;
+  const bool active = k0 < T_;
+  const T* base = qkv + (int64_t)b * T_ * S3;
+  const int kv = k0 + lr;
+
+  F kf[ND], vf[ND];
+  if (active) {
+#pragma unroll
+    for (int ds = 0; ds < ND; ds++) {
+      kf[ds] = ld8(base + (int64_t)kv * S3 + C + h * HD + ds * 16 + 8 * lg);
+      vf[ds] = ld8(base + (int64_t)kv * S3 + 2 * C + h * HD + ds * 16 + 8 * lg);
+    }
+  }
+  f32x16 dk[NDT], dv[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; dt++) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+  const float* lrow = lse + ((int64_t)b * NH + h) * T_;
+  const float* drow = dsum + ((int64_t)b * NH + h) * T_;
+
+  const int q_begin = (kblk * NW * WQ / KT) * KT;
+  for (int qt0 = q_begin; qt0 < T_; qt0 += KT) {
+    __syncthreads();
+    load_rows<T, HD>(Qs, base + (int64_t)qt0 * S3 + h * HD, S3, tid);
+    load_rows<T, HD>(Ds, dout + ((int64_t)b * T_ + qt0) * C + h * HD, C, tid);
+    load_rows_t<T, HD>(Qt, base + (int64_t)qt0 * S3 + h * HD, S3, tid);
+    load_rows_t<T, HD>(Dt, dout + ((int64_t)b * T_ + qt0) * C + h * HD, C, tid);
+    if (tid < KT) {
+      Ls[tid] = lrow[qt0 + tid] * LOG2E;
+      Dd[tid] = drow[qt0 + tid];
+    }
+    __syncthreads();
+    if (!active || qt0 + KT - 1 < k0) continue;
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int c2 = 0; c2 < 2; c2++) {
+      s[c2] = f32x16{};
+      dp[c2] = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < ND; ds++) {
+        mma16(s[c2], ld8(Qs + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), kf[ds]);
+        mma16(dp[c2], ld8(Ds + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), vf[ds]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int ql = c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+        const float p = qt0 + ql >= kv ? exp2f(s[c2][r] * sl2 - Ls[ql]) : 0.f;
+        s[c2][r] = p;
+        dp[c2][r] = p * (dp[c2][r] - Dd[ql]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < KT / 16; c++) {
+      const F pf = acc_frag<T>(s[c / 2], c % 2);
+      const F sf = acc_frag<T>(dp[c / 2], c % 2);
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++) {
+        mma16(dv[dt], ld_split(Dt, LDV, dt * 32 + lr, c, lg), pf);
+        mma16(dk[dt], ld_split(Qt, LDV, dt * 32 + lr, c, lg), sf);
+      }
+    }
+  }
+  if (!active) return;
+  T* row = dqkv + ((int64_t)b * T_ + kv) * S3 + h * HD;
+#pragma unroll
+  for (int dt = 0; dt < NDT; dt++)
+#pragma unroll
+    for (int qq = 0; qq < 4; qq++) {
+      Q vk, vv;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        vk[e] = from_f<T>(dk[dt][4 * qq + e] * scale);
+        vv[e] = from_f<T>(dv[dt][4 * qq + e]);
+      }
+      *reinterpret_cast<Q*>(row + C + dt * 32 + 8 * qq + 4 * lg) = vk;
+      *reinterpret_cast<Q*>(row + 2 * C + dt * 32 + 8 * qq + 4 * lg) = vv;
+    }
+}
+
+template <typename T, int HD>
+hipError_t fwd_t(hipStream_t st, const void* qkv, void* out, float* lse, int B, int T_, int NH) {
+  dim3 grid((T_ + NW * WQ - 1) / (NW * WQ), NH, B);
+  const float sl2 = LOG2E / sqrtf((float)HD);
+  hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(qkv),
+                     static_cast<T*>(out), lse, T_, NH, sl2);
+  return hipGetLastError();
+}
+
+template <typename T, int HD>
+hipError_t dsum_t(hipStream_t st, const void* out, const void* dout, float* dsum, int B, int T_, int NH) {
+  const int64_t n = (int64_t)B * T_ * NH;
+  hipLaunchKernelGGL((attn_dsum_kernel<T, HD>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                     static_cast<const T*>(out), static_cast<const T*>(dout), dsum, T_, NH, n);
+  return hipGetLastError();
+}
+
+template <typename T, int HD, bool DQ>
+hipError_t bwd_t(hipStream_t st, const void* qkv, const void* dout, const float* lse, const float* dsum, void* dqkv,
+                 int B, int T_, int NH) {
+  dim3 grid((T_ + NW * WQ - 1) / (NW * WQ), NH, B);
+  const float scale = 1.f / sqrtf((float)HD), sl2 = LOG2E * scale;
+  if (DQ)
+    hipLaunchKernelGGL((attn_dq_kernel<T, HD>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(qkv),
+                       static_cast<const T*>(dout), lse, dsum, static_cast<T*>(dqkv), T_, NH, sl2, scale);
+  else
+    hipLaunchKernelGGL((attn_dkv_kernel<T, HD>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(qkv),
+                       static_cast<const T*>(dout), lse, dsum, static_cast<T*>(dqkv), T_, NH, sl2, scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t attn_fwd(hipStream_t st, Prec p, const void* qkv, void* out, float* lse, int B, int T_, int NH, int hd) {
+  if (T_ % KT != 0) return hipErrorInvalidValue;
+  if (p == BF16) {
+    if (hd == 64) return fwd_t<bf16, 64>(st, qkv, out, lse, B, T_, NH);
+    if (hd == 32) return fwd_t<bf16, 32>(st, qkv, out, lse, B, T_, NH);
+  } else {
+    if (hd == 64) return fwd_t<float, 64>(st, qkv, out, lse, B, T_, NH);
+    if (hd == 32) return fwd_t<float, 32>(st, qkv, out, lse, B, T_, NH);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t attn_bwd_dsum(hipStream_t st, Prec p, const void* out, const void* dout, float* dsum, int B, int T_, int NH,
+                         int hd) {
+  if (p == BF16) {
+    if (hd == 64) return dsum_t<bf16, 64>(st, out, dout, dsum, B, T_, NH);
+    if (hd == 32) return dsum_t<bf16, 32>(st, out, dout, dsum, B, T_, NH);
+  } else {
+    if (hd == 64) return dsum_t<float, 64>(st, out, dout, dsum, B, T_, NH);
+    if (hd == 32) return dsum_t<float, 32>(st, out, dout, dsum, B, T_, NH);
+  }
+  return hipErrorInvalidValue;
+}
+
+#define ATTN_BWD_DISPATCH(DQ)                                                                   \
+  if (T_ % KT != 0) return hipErrorInvalidValue;                                                \
+  if (p == BF16) {                                                                              \
+    if (hd == 64) return bwd_t<bf16, 64, DQ>(st, qkv, dout, lse, dsum, dqkv, B, T_, NH);        \
+    if (hd == 32) return bwd_t<bf16, 32, DQ>(st, qkv, dout, lse, dsum, dqkv, B, T_, NH);        \
+  } else {                                                                                      \
+    if (hd == 64) return bwd_t<float, 64, DQ>(st, qkv, dout, lse, dsum, dqkv, B, T_, NH);       \
+    if (hd == 32) return bwd_t<float, 32, DQ>(st, qkv, dout, lse, dsum, dqkv, B, T_, NH);       \
+  }                                                                                             \
+  return hipErrorInvalidValue;
+
+hipError_t attn_bwd_dkv(hipStream_t st, Prec p, const void* qkv, const void* dout, const float* lse, const float* dsum,
+                        void* dqkv, int B, int T_, int NH, int hd) {
+  ATTN_BWD_DISPATCH(false)
+}
+
+hipError_t attn_bwd_dq(hipStream_t st, Prec p, const void* qkv, const void* dout, const float* lse, const float* dsum,
+                       void* dqkv, int B, int T_, int NH, int hd) {
+  ATTN_BWD_DISPATCH(true)
+}
+#undef ATTN_BWD_DISPATCH
+
+}  // namespace gpt2k

@@ -1,0 +1,84 @@
+// common.h -- device helpers shared by the gfx950 kernels of the GPT-2 step.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Eight consecutive elements along a matmul's reduction dimension: the
+// per-lane operand of one (virtual) 32x32x16 MFMA step.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { typedef bf16x8 type; };
+template <> struct Frag<float> { typedef f32x8 type; };
+
+// Four consecutive output elements (one lane's run in a 32x32 accumulator).
+template <typename T> struct Quad;
+template <> struct Quad<bf16> { typedef bf16x4 type; };
+template <> struct Quad<float> { typedef f32x4 type; };
+
+__device__ __forceinline__ bf16x8 ld8(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x8 ld8(const float* p) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  return f32x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ void st8(bf16* p, bf16x8 v) { *reinterpret_cast<bf16x8*>(p) = v; }
+__device__ __forceinline__ void st8(float* p, f32x8 v) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
+// One 32x32x16 product: acc[32x32] += A(32 rows x 16 k) * B(16 k x 32 cols).
+// Lane l holds row/col l%32 of its operand and 8 of the 16 k values; which 8
+// is fixed by the lane group g = l/32 and the slot, identically for A and B,
+// so the sum runs over all 16.  Accumulator element r of lane l sits at
+// row 8*(r/4) + 4*(l/32) + r%4, col l%32 (layout checked on gfx950).
+__device__ __forceinline__ void mma16(f32x16& acc, bf16x8 a, bf16x8 b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+// fp32: eight 32x32x2 MFMAs; MFMA s pairs slot s of lane group 0 with slot s
+// of lane group 1 (its two k values), so all 16 (group, slot) pairs are summed.
+__device__ __forceinline__ void mma16(f32x16& acc, f32x8 a, f32x8 b) {
+#pragma unroll
+  for (int s = 0; s < 8; s++) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x) { return (T)x; }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// tanh-approximate GELU and its derivative ("Karpathy's four-hour GPT-2
+// reproduction in one post", what I checked myself: GPT-2 uses the tanh form).
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k = 0.7978845608028654f;  // sqrt(2/pi)
+  float t = tanhf(k * (x + 0.044715f * x * x * x));
+  return 0.5f * x * (1.0f + t);
+}
+__device__ __forceinline__ float gelu_tanh_grad(float x) {
+  const float k = 0.7978845608028654f;
+  float t = tanhf(k * (x + 0.044715f * x * x * x));
+  return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * k * (1.0f + 3.0f * 0.044715f * x * x);
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Renumber so each XCD gets one contiguous range of logical block ids, which
+// keeps neighbouring tiles (sharing operand panels) in the same L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  if (nblocks % 8 != 0) return bid;
+  return (bid % 8) * (nblocks / 8) + bid / 8;
+}

@@ -1,0 +1,756 @@
+// gpt2.hip -- host side of the library: shape checks, flat parameter layout,
+// workspace plan, the kernel sequence of one training step, and the C ABI
+// declared in include/gpt2.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "gpt2.h"
+#include "kernels.h"
+
+using namespace gpt2k;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Parameter layout.  The GPT-2 tensors ("Karpathy's four-hour GPT-2
+// reproduction in one post", part 1: HF-compatible names, embedding tied to
+// the output layer), 2-D tensors first so weight decay covers one prefix.
+// ---------------------------------------------------------------------------
+enum TensorKind { T_WTE, T_WPE, T_QKVW, T_PROJW, T_FCW, T_FCPW, T_LN1G, T_LN1B, T_QKVB, T_PROJB, T_LN2G, T_LN2B,
+                  T_FCB, T_FCPB, T_LNFG, T_LNFB };
+
+struct Tensor {
+  std::string name;
+  int kind, layer;
+  int64_t offset;
+  int rows, cols;
+  int decay;
+};
+
+struct Layout {
+  std::vector<Tensor> t;
+  int64_t total = 0, n_decay = 0;
+};
+
+Layout make_layout(const gpt2_config_t& c) {
+  Layout L;
+  const int C = c.n_embd;
+  auto add = [&](const char* nm, int kind, int layer, int rows, int cols) {
+    Tensor x;
+    x.name = layer >= 0 ? "h." + std::to_string(layer) + "." + nm : nm;
+    x.kind = kind;
+    x.layer = layer;
+    x.offset = L.total;
+    x.rows = rows;
+    x.cols = cols;
+    x.decay = cols > 0;
+    L.total += (int64_t)rows * (cols > 0 ? cols : 1);
+    if (x.decay) L.n_decay = L.total;
+    L.t.push_back(x);
+  };
+  add("wte", T_WTE, -1, c.padded_vocab_size, C);
+  add("wpe", T_WPE, -1, c.max_seq_len, C);
+  for (int l = 0; l < c.n_layer; l++) {
+    add("attn.c_attn.weight", T_QKVW, l, 3 * C, C);
+    add("attn.c_proj.weight", T_PROJW, l, C, C);
+    add("mlp.c_fc.weight", T_FCW, l, 4 * C, C);
+    add("mlp.c_proj.weight", T_FCPW, l, C, 4 * C);
+  }
+  for (int l = 0; l < c.n_layer; l++) {
+    add("ln_1.weight", T_LN1G, l, C, 0);
+    add("ln_1.bias", T_LN1B, l, C, 0);
+    add("attn.c_attn.bias", T_QKVB, l, 3 * C, 0);
+    add("attn.c_proj.bias", T_PROJB, l, C, 0);
+    add("ln_2.weight", T_LN2G, l, C, 0);
+    add("ln_2.bias", T_LN2B, l, C, 0);
+    add("mlp.c_fc.bias", T_FCB, l, 4 * C, 0);
+    add("mlp.c_proj.bias", T_FCPB, l, C, 0);
+  }
+  add("ln_f.weight", T_LNFG, -1, C, 0);
+  add("ln_f.bias", T_LNFB, -1, C, 0);
+  return L;
+}
+
+int check_config(const gpt2_config_t* c) {
+  if (!c) return GPT2_ERR_ARG;
+  if (c->vocab_size <= 0 || c->vocab_size > (1 << 24) || c->padded_vocab_size < c->vocab_size ||
+      c->padded_vocab_size % 128 != 0 || c->n_layer <= 0 || c->n_head <= 0 || c->n_embd <= 0 ||
+      c->n_embd % c->n_head != 0 || c->n_embd % 128 != 0 || c->n_embd > 2048 || c->max_seq_len <= 0)
+    return GPT2_ERR_CONFIG;
+  const int hd = c->n_embd / c->n_head;
+  if (hd != 32 && hd != 64) return GPT2_ERR_CONFIG;
+  return GPT2_OK;
+}
+
+int check_bt(const gpt2_config_t* c, int B, int T) {
+  if (B <= 0 || T <= 0 || T % 64 != 0 || T > c->max_seq_len || ((int64_t)B * T) % 128 != 0 ||
+      (int64_t)B * T > (1 << 26))
+    return GPT2_ERR_SHAPE;
+  return GPT2_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace plan: byte offsets (256-aligned) of every device scratch array.
+// ---------------------------------------------------------------------------
+struct Plan {
+  int64_t bytes = 0;
+  // per layer
+  std::vector<int64_t> x_in, x_mid, h1, h2, mean1, rstd1, mean2, rstd2, qkv, atty, lse, u, g;
+  int64_t hf, meanf, rstdf, logits, loss_rows, loss_tmp;
+  int64_t dres, dres_lp, dh, datty, dqkv, du, dsum, piece;
+  int64_t wpart, lnpart, cspart, normpart;
+  int64_t ska, sva, skb, svb, seg, nseg;
+  int64_t flags, scale, norm;
+  int cs_chunks;
+  std::vector<int> split;  // split-K factor per layer weight kind (qkv, proj, fc, fcproj)
+};
+
+constexpr int GEMM_BK_MIN = 64;
+
+int pick_splits(int tiles, int M) {
+  // enough blocks to cover the chip twice; the reduction length M must split
+  // into equal multiples of 64
+  int s = 1;
+  while (s < 16 && tiles * s < 512 && (M % (2 * s * GEMM_BK_MIN)) == 0) s *= 2;
+  return s;
+}
+
+Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
+  Plan P;
+  const int64_t M = (int64_t)B * T, C = c.n_embd, L = c.n_layer, NH = c.n_head;
+  const int64_t a = prec == GPT2_BF16 ? 2 : 4;
+  auto take = [&](int64_t bytes) {
+    const int64_t off = P.bytes;
+    P.bytes += (bytes + 255) / 256 * 256;
+    return off;
+  };
+  for (int64_t l = 0; l <= L; l++) P.x_in.push_back(take(4 * M * C));
+  for (int64_t l = 0; l < L; l++) {
+    P.x_mid.push_back(take(4 * M * C));
+    P.h1.push_back(take(a * M * C));
+    P.h2.push_back(take(a * M * C));
+    P.mean1.push_back(take(4 * M));
+    P.rstd1.push_back(take(4 * M));
+    P.mean2.push_back(take(4 * M));
+    P.rstd2.push_back(take(4 * M));
+    P.qkv.push_back(take(a * M * 3 * C));
+    P.atty.push_back(take(a * M * C));
+    P.lse.push_back(take(4 * M * NH));
+    P.u.push_back(take(a * M * 4 * C));
+    P.g.push_back(take(a * M * 4 * C));
+  }
+  P.hf = take(a * M * C);
+  P.meanf = take(4 * M);
+  P.rstdf = take(4 * M);
+  P.logits = take(a * M * c.padded_vocab_size);
+  P.loss_rows = take(4 * M);
+  P.loss_tmp = take(4);
+  P.dres = take(4 * M * C);
+  P.dres_lp = prec == GPT2_BF16 ? take(a * M * C) : P.dres;
+  P.dh = take(a * M * C);
+  P.datty = take(a * M * C);
+  P.dqkv = take(a * M * 3 * C);
+  P.du = take(a * M * 4 * C);
+  P.dsum = take(4 * M * NH);
+  P.piece = take(4 * M * C);
+  const int tq = (int)((3 * C / 128) * (C / 128)), tp = (int)((C / 128) * (C / 128)), tf = (int)((4 * C / 128) * (C / 128));
+  P.split = {pick_splits(tq, (int)M), pick_splits(tp, (int)M), pick_splits(tf, (int)M), pick_splits(tf, (int)M)};
+  int64_t wmax = 0;
+  const int64_t wsz[4] = {3 * C * C, C * C, 4 * C * C, 4 * C * C};
+  for (int k = 0; k < 4; k++) wmax = std::max(wmax, (int64_t)P.split[k] * wsz[k]);
+  P.wpart = take(4 * wmax);
+  P.lnpart = take(4 * (int64_t)layernorm_bwd_parts((int)M) * 2 * C);
+  P.cs_chunks = (int)std::min<int64_t>(256, M);
+  P.cspart = take(4 * (int64_t)P.cs_chunks * 4 * C);
+  P.normpart = take(8 * (int64_t)grad_norm_parts());
+  P.ska = take(4 * M);
+  P.sva = take(4 * M);
+  P.skb = take(4 * M);
+  P.svb = take(4 * M);
+  P.seg = take(4 * (M + 1));
+  P.nseg = take(4);
+  P.flags = take(16);
+  P.scale = take(4);
+  P.norm = take(4);
+  return P;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel timing (HIP events on the library's stream around selected launches)
+// ---------------------------------------------------------------------------
+struct TimedLaunch {
+  hipEvent_t a, b;
+  double flops;
+};
+
+}  // namespace
+
+struct gpt2_handle {
+  gpt2_config_t cfg;
+  Prec prec;
+  int B, T;
+  int64_t M;
+  float *params, *grads, *m, *v;
+  void* params_lp;
+  char* ws;
+  hipStream_t st;
+  Layout lay;
+  Plan plan;
+  std::vector<const Tensor*> by_kind_layer;  // [kind * (L+1) + layer+1]
+  bool have_fwd = false, fwd_has_targets = false;
+  std::string err;
+  int timed = -1;
+  std::vector<TimedLaunch> timings;
+
+  template <typename X> X* w(int64_t off) { return reinterpret_cast<X*>(ws + off); }
+  const Tensor& tensor(int kind, int layer) const { return *by_kind_layer[kind * (cfg.n_layer + 1) + layer + 1]; }
+  float* P32(int kind, int layer = -1) { return params + tensor(kind, layer).offset; }
+  float* G32(int kind, int layer = -1) { return grads + tensor(kind, layer).offset; }
+  // matmul operand copy of a weight: bf16 copy in BF16, the master in FP32
+  const void* W(int kind, int layer = -1) {
+    const int64_t off = tensor(kind, layer).offset;
+    return prec == BF16 ? static_cast<const void*>(static_cast<const uint16_t*>(params_lp) + off)
+                        : static_cast<const void*>(params + off);
+  }
+  int64_t act_bytes() const { return prec == BF16 ? 2 : 4; }
+};
+
+namespace {
+
+int fail(gpt2_t* h, int code, const std::string& msg) {
+  if (h) h->err = msg;
+  return code;
+}
+
+int hip_check(gpt2_t* h, hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(h, GPT2_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return GPT2_OK;
+}
+
+// Brackets one launch with events when its kernel id is being timed.
+struct Timer {
+  gpt2_t* h;
+  bool on;
+  TimedLaunch tl;
+  Timer(gpt2_t* h_, int id, double flops) : h(h_), on(h_->timed == id) {
+    if (on) {
+      tl.flops = flops;
+      (void)hipEventCreate(&tl.a);
+      (void)hipEventCreate(&tl.b);
+      (void)hipEventRecord(tl.a, h->st);
+    }
+  }
+  void done() {
+    if (on) {
+      (void)hipEventRecord(tl.b, h->st);
+      h->timings.push_back(tl);
+      on = false;
+    }
+  }
+  ~Timer() { done(); }
+};
+
+}  // namespace
+
+// Kernel ids for timing (one per kernel function).
+enum {
+  K_GEMM_NT_STORE = 0,
+  K_GEMM_NT_GELU,
+  K_GEMM_NT_RESID,
+  K_GEMM_NN_STORE,
+  K_GEMM_NN_GELU_BWD,
+  K_GEMM_TN_F32,
+  K_ATTN_FWD,
+  K_ATTN_DKV,
+  K_ATTN_DQ,
+  K_CE,
+  K_LN_FWD,
+  K_LN_BWD,
+  K_ADAMW,
+  K_COUNT
+};
+static const char* const kKernelNames[K_COUNT] = {
+    "gemm_nt_store", "gemm_nt_gelu", "gemm_nt_resid", "gemm_nn_store", "gemm_nn_gelu_bwd", "gemm_tn_f32",
+    "attn_fwd",      "attn_bwd_dkv", "attn_bwd_dq",   "cross_entropy", "layernorm_fwd",     "layernorm_bwd",
+    "adamw"};
+
+namespace {
+
+int run_gemm(gpt2_t* h, int kid, int a_t, int b_t, int epi, const GemmArgs& g, const char* what) {
+  Timer t(h, kid, 2.0 * g.M * g.N * g.K);
+  hipError_t e = gemm(h->st, h->prec, a_t, b_t, epi, g);
+  t.done();
+  return hip_check(h, e, what);
+}
+
+// Forward-layer matmul: out = X W^T (+ epilogue); X [M, K] row-major, W [N, K].
+GemmArgs fwd_args(gpt2_t* h, const void* X, const void* W, int N, int K, void* out, const float* bias) {
+  GemmArgs g;
+  g.A = X;
+  g.lda = K;
+  g.B = W;
+  g.ldb = K;
+  g.M = (int)h->M;
+  g.N = N;
+  g.K = K;
+  g.C = out;
+  g.ldc = N;
+  g.bias = bias;
+  return g;
+}
+
+// Input gradient: out [M, K] = dY [M, N] W [N, K].
+GemmArgs dx_args(gpt2_t* h, const void* dY, const void* W, int N, int K, void* out) {
+  GemmArgs g;
+  g.A = dY;
+  g.lda = N;
+  g.B = W;
+  g.ldb = K;
+  g.M = (int)h->M;
+  g.N = K;
+  g.K = N;
+  g.C = out;
+  g.ldc = K;
+  return g;
+}
+
+// Weight gradient of W [N, K]: dW (+)= dY^T X, dY [M, N], X [M, K]; split-K
+// partials are reduced in order into the gradient buffer.
+int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* dW, int splits, int accumulate,
+                const char* what) {
+  GemmArgs g;
+  g.A = dY;
+  g.lda = N;
+  g.B = X;
+  g.ldb = K;
+  g.M = N;
+  g.N = K;
+  g.K = (int)h->M;
+  g.splits = splits;
+  if (splits == 1) {
+    g.C = dW;
+    g.ldc = K;
+    g.accumulate = accumulate;
+    return run_gemm(h, K_GEMM_TN_F32, 1, 1, EPI_F32, g, what);
+  }
+  float* part = h->w<float>(h->plan.wpart);
+  g.C = part;
+  g.ldc = K;
+  g.split_stride = (int64_t)N * K;
+  int rc = run_gemm(h, K_GEMM_TN_F32, 1, 1, EPI_F32, g, what);
+  if (rc) return rc;
+  return hip_check(h, reduce_parts(h->st, part, splits, (int64_t)N * K, dW, N * K, accumulate), "reduce dW");
+}
+
+int bias_grad(gpt2_t* h, const void* dY, int x_is_f32, int N, float* db, int accumulate) {
+  float* part = h->w<float>(h->plan.cspart);
+  int rc = hip_check(h, colsum_parts(h->st, h->prec, x_is_f32, dY, (int)h->M, N, part, h->plan.cs_chunks), "colsum");
+  if (rc) return rc;
+  return hip_check(h, reduce_parts(h->st, part, h->plan.cs_chunks, N, db, N, accumulate), "reduce db");
+}
+
+int ln_backward(gpt2_t* h, const void* dy, const float* x, const float* mean, const float* rstd, int kind_g, int layer,
+                int accumulate_dres, int accumulate_grads) {
+  const int C = h->cfg.n_embd, M = (int)h->M;
+  float* part = h->w<float>(h->plan.lnpart);
+  int nparts = 0;
+  void* dres_lp = h->prec == BF16 ? h->w<void>(h->plan.dres_lp) : nullptr;
+  Timer t(h, K_LN_BWD, 0);
+  hipError_t e = layernorm_bwd(h->st, h->prec, dy, x, mean, rstd, h->P32(kind_g, layer), h->w<float>(h->plan.dres),
+                               dres_lp, accumulate_dres, part, M, C, &nparts);
+  t.done();
+  int rc = hip_check(h, e, "layernorm_bwd");
+  if (rc) return rc;
+  // gain and bias gradients are adjacent in the layout: one reduction covers both
+  return hip_check(h, reduce_parts(h->st, part, nparts, 2 * C, h->G32(kind_g, layer), 2 * C, accumulate_grads),
+                   "reduce ln");
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t gpt2_num_params(const gpt2_config_t* cfg) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  return make_layout(*cfg).total;
+}
+
+int64_t gpt2_num_decay_params(const gpt2_config_t* cfg) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  return make_layout(*cfg).n_decay;
+}
+
+int gpt2_param_layout(const gpt2_config_t* cfg, gpt2_tensor_desc_t* out, int cap) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  Layout L = make_layout(*cfg);
+  if (out)
+    for (int i = 0; i < (int)L.t.size() && i < cap; i++) {
+      memset(&out[i], 0, sizeof(out[i]));
+      snprintf(out[i].name, sizeof(out[i].name), "%s", L.t[i].name.c_str());
+      out[i].offset = L.t[i].offset;
+      out[i].rows = L.t[i].rows;
+      out[i].cols = L.t[i].cols;
+      out[i].decay = L.t[i].decay;
+    }
+  return (int)L.t.size();
+}
+
+int gpt2_check_shapes(const gpt2_config_t* cfg, int B, int T) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  return check_bt(cfg, B, T);
+}
+
+int64_t gpt2_workspace_bytes(const gpt2_config_t* cfg, int B, int T, int precision) {
+  int rc = gpt2_check_shapes(cfg, B, T);
+  if (rc) return rc;
+  if (precision != GPT2_FP32 && precision != GPT2_BF16) return GPT2_ERR_ARG;
+  return make_plan(*cfg, B, T, precision).bytes;
+}
+
+int gpt2_init(gpt2_t** out, const gpt2_config_t* cfg, int precision, int B, int T, float* params, void* params_lp,
+              float* grads, float* adam_m, float* adam_v, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!out) return GPT2_ERR_ARG;
+  *out = nullptr;
+  int rc = gpt2_check_shapes(cfg, B, T);
+  if (rc) return rc;
+  if (precision != GPT2_FP32 && precision != GPT2_BF16) return GPT2_ERR_ARG;
+  auto aligned = [](const void* p) { return p && (reinterpret_cast<uintptr_t>(p) % 256) == 0; };
+  if (!aligned(params) || !aligned(grads) || !aligned(adam_m) || !aligned(adam_v) || !aligned(workspace))
+    return GPT2_ERR_ARG;
+  if (precision == GPT2_BF16 && !aligned(params_lp)) return GPT2_ERR_ARG;
+  Plan plan = make_plan(*cfg, B, T, precision);
+  if (workspace_bytes < plan.bytes) return GPT2_ERR_WORKSPACE;
+  gpt2_t* h = new (std::nothrow) gpt2_handle();
+  if (!h) return GPT2_ERR_ARG;
+  h->cfg = *cfg;
+  h->prec = precision == GPT2_BF16 ? BF16 : F32;
+  h->B = B;
+  h->T = T;
+  h->M = (int64_t)B * T;
+  h->params = params;
+  h->params_lp = precision == GPT2_BF16 ? params_lp : nullptr;
+  h->grads = grads;
+  h->m = adam_m;
+  h->v = adam_v;
+  h->ws = static_cast<char*>(workspace);
+  h->st = static_cast<hipStream_t>(stream);
+  h->lay = make_layout(*cfg);
+  h->plan = plan;
+  h->by_kind_layer.assign(16 * (cfg->n_layer + 1), nullptr);
+  for (auto& t : h->lay.t) h->by_kind_layer[t.kind * (cfg->n_layer + 1) + t.layer + 1] = &t;
+  // the deferred status flags live in the caller's workspace: start them at zero
+  if (hipMemsetAsync(h->w<int>(plan.flags), 0, 16, h->st) != hipSuccess) {
+    delete h;
+    return GPT2_ERR_HIP;
+  }
+  *out = h;
+  return GPT2_OK;
+}
+
+void gpt2_destroy(gpt2_t* h) {
+  if (!h) return;
+  for (auto& t : h->timings) {
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
+  }
+  delete h;
+}
+
+int gpt2_set_stream(gpt2_t* h, void* stream) {
+  if (!h) return GPT2_ERR_ARG;
+  h->st = static_cast<hipStream_t>(stream);
+  return GPT2_OK;
+}
+
+int gpt2_refresh_params(gpt2_t* h) {
+  if (!h) return GPT2_ERR_ARG;
+  if (h->prec != BF16) return GPT2_OK;
+  return hip_check(h, to_bf16(h->st, h->params, h->params_lp, h->lay.total), "to_bf16");
+}
+
+int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, float* d_loss, float* d_loss_rows) {
+  if (!h || !d_idx) return fail(h, GPT2_ERR_ARG, "null handle or ids");
+  const gpt2_config_t& c = h->cfg;
+  const int C = c.n_embd, L = c.n_layer, NH = c.n_head, hd = C / NH, Mi = (int)h->M;
+  const Plan& P = h->plan;
+  const int64_t Mx = h->M;
+  int rc;
+  int* flags = h->w<int>(P.flags);
+  h->have_fwd = false;
+
+  rc = hip_check(h, embed_fwd(h->st, d_idx, d_targets, h->P32(T_WTE), h->P32(T_WPE), h->w<float>(P.x_in[0]), h->B, h->T, C,
+                              c.vocab_size, flags),
+                 "embed_fwd");
+  if (rc) return rc;
+  if (d_targets) {
+    rc = hip_check(h, embed_sort(h->st, d_idx, Mi, c.vocab_size, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva),
+                                 h->w<int32_t>(P.skb), h->w<int32_t>(P.svb), h->w<int32_t>(P.seg), h->w<int32_t>(P.nseg)),
+                   "embed_sort");
+    if (rc) return rc;
+  }
+  for (int l = 0; l < L; l++) {
+    {
+      Timer t(h, K_LN_FWD, 0);
+      rc = hip_check(h, layernorm_fwd(h->st, h->prec, h->w<float>(P.x_in[l]), h->P32(T_LN1G, l), h->P32(T_LN1B, l),
+                                      h->w<void>(P.h1[l]), h->w<float>(P.mean1[l]), h->w<float>(P.rstd1[l]), Mi, C),
+                     "ln1");
+    }
+    if (rc) return rc;
+    GemmArgs g = fwd_args(h, h->w<void>(P.h1[l]), h->W(T_QKVW, l), 3 * C, C, h->w<void>(P.qkv[l]), h->P32(T_QKVB, l));
+    if ((rc = run_gemm(h, K_GEMM_NT_STORE, 0, 0, EPI_STORE, g, "qkv"))) return rc;
+    {
+      const double pairs = (double)h->B * NH * ((double)h->T * (h->T + 1) / 2);
+      Timer t(h, K_ATTN_FWD, 4.0 * hd * pairs);
+      rc = hip_check(h, attn_fwd(h->st, h->prec, h->w<void>(P.qkv[l]), h->w<void>(P.atty[l]), h->w<float>(P.lse[l]),
+                                 h->B, h->T, NH, hd),
+                     "attn_fwd");
+    }
+    if (rc) return rc;
+    g = fwd_args(h, h->w<void>(P.atty[l]), h->W(T_PROJW, l), C, C, h->w<void>(P.x_mid[l]), h->P32(T_PROJB, l));
+    g.resid = h->w<float>(P.x_in[l]);
+    g.ldr = C;
+    if ((rc = run_gemm(h, K_GEMM_NT_RESID, 0, 0, EPI_RESID, g, "proj"))) return rc;
+    {
+      Timer t(h, K_LN_FWD, 0);
+      rc = hip_check(h, layernorm_fwd(h->st, h->prec, h->w<float>(P.x_mid[l]), h->P32(T_LN2G, l), h->P32(T_LN2B, l),
+                                      h->w<void>(P.h2[l]), h->w<float>(P.mean2[l]), h->w<float>(P.rstd2[l]), Mi, C),
+                     "ln2");
+    }
+    if (rc) return rc;
+    g = fwd_args(h, h->w<void>(P.h2[l]), h->W(T_FCW, l), 4 * C, C, h->w<void>(P.g[l]), h->P32(T_FCB, l));
+    g.aux = h->w<void>(P.u[l]);
+    g.ldaux = 4 * C;
+    if ((rc = run_gemm(h, K_GEMM_NT_GELU, 0, 0, EPI_GELU, g, "fc"))) return rc;
+    g = fwd_args(h, h->w<void>(P.g[l]), h->W(T_FCPW, l), C, 4 * C, h->w<void>(P.x_in[l + 1]), h->P32(T_FCPB, l));
+    g.resid = h->w<float>(P.x_mid[l]);
+    g.ldr = C;
+    if ((rc = run_gemm(h, K_GEMM_NT_RESID, 0, 0, EPI_RESID, g, "fcproj"))) return rc;
+  }
+  {
+    Timer t(h, K_LN_FWD, 0);
+    rc = hip_check(h, layernorm_fwd(h->st, h->prec, h->w<float>(P.x_in[L]), h->P32(T_LNFG), h->P32(T_LNFB),
+                                    h->w<void>(P.hf), h->w<float>(P.meanf), h->w<float>(P.rstdf), Mi, C),
+                   "lnf");
+  }
+  if (rc) return rc;
+  // tied output layer over the padded vocabulary
+  GemmArgs g = fwd_args(h, h->w<void>(P.hf), h->W(T_WTE), c.padded_vocab_size, C, h->w<void>(P.logits), nullptr);
+  if ((rc = run_gemm(h, K_GEMM_NT_STORE, 0, 0, EPI_STORE, g, "lm_head"))) return rc;
+  if (d_targets) {
+    float* rows = d_loss_rows ? d_loss_rows : h->w<float>(P.loss_rows);
+    {
+      Timer t(h, K_CE, 0);
+      // dlogits of the mean loss; the 1/K of gradient accumulation is applied in backward
+      rc = hip_check(h, cross_entropy(h->st, h->prec, h->w<void>(P.logits), d_targets, rows, Mi, c.vocab_size,
+                                      c.padded_vocab_size, 1.0f / (float)Mx, 1),
+                     "cross_entropy");
+    }
+    if (rc) return rc;
+    if (d_loss) {
+      rc = hip_check(h, mean_loss(h->st, rows, Mi, d_loss), "mean_loss");
+      if (rc) return rc;
+    }
+  }
+  h->have_fwd = true;
+  h->fwd_has_targets = d_targets != nullptr;
+  return GPT2_OK;
+}
+
+int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
+  if (!h) return GPT2_ERR_ARG;
+  if (grad_accum_steps < 1 || micro_step < 0 || micro_step >= grad_accum_steps)
+    return fail(h, GPT2_ERR_ARG, "bad micro_step / grad_accum_steps");
+  if (!h->have_fwd || !h->fwd_has_targets) return fail(h, GPT2_ERR_ARG, "backward needs a forward with targets");
+  const gpt2_config_t& c = h->cfg;
+  const int C = c.n_embd, L = c.n_layer, NH = c.n_head, hd = C / NH, Vp = c.padded_vocab_size;
+  const Plan& P = h->plan;
+  const int acc = micro_step > 0;
+  const float alpha = 1.0f / (float)grad_accum_steps;
+  const bool lp = h->prec == BF16;
+  void* dres_op = lp ? h->w<void>(P.dres_lp) : h->w<void>(P.dres);  // matmul operand view of dres
+  float* dres = h->w<float>(P.dres);
+  int rc;
+
+  // tied output layer: dhf = dlogits wte ; dwte (+)= dlogits^T hf   (both scaled by 1/K)
+  GemmArgs g = dx_args(h, h->w<void>(P.logits), h->W(T_WTE), Vp, C, h->w<void>(P.dh));
+  g.alpha = alpha;
+  if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "lm_head dx"))) return rc;
+  {
+    GemmArgs w;
+    w.A = h->w<void>(P.logits);
+    w.lda = Vp;
+    w.B = h->w<void>(P.hf);
+    w.ldb = C;
+    w.M = Vp;
+    w.N = C;
+    w.K = (int)h->M;
+    w.C = h->G32(T_WTE);
+    w.ldc = C;
+    w.accumulate = acc;
+    w.alpha = alpha;
+    if ((rc = run_gemm(h, K_GEMM_TN_F32, 1, 1, EPI_F32, w, "lm_head dw"))) return rc;
+  }
+  if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[L]), h->w<float>(P.meanf), h->w<float>(P.rstdf), T_LNFG,
+                        -1, 0, acc)))
+    return rc;
+
+  for (int l = L - 1; l >= 0; l--) {
+    // MLP down-projection: dres is the gradient of the block output
+    if ((rc = bias_grad(h, dres, 1, C, h->G32(T_FCPB, l), acc))) return rc;
+    if ((rc = weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), P.split[3], acc, "fcproj dw")))
+      return rc;
+    g = dx_args(h, dres_op, h->W(T_FCPW, l), C, 4 * C, h->w<void>(P.du));
+    g.aux = h->w<void>(P.u[l]);
+    g.ldaux = 4 * C;
+    if ((rc = run_gemm(h, K_GEMM_NN_GELU_BWD, 0, 1, EPI_GELU_BWD, g, "fcproj dx"))) return rc;
+    // MLP up-projection
+    if ((rc = bias_grad(h, h->w<void>(P.du), 0, 4 * C, h->G32(T_FCB, l), acc))) return rc;
+    if ((rc = weight_grad(h, h->w<void>(P.du), h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), P.split[2], acc,
+                          "fc dw")))
+      return rc;
+    g = dx_args(h, h->w<void>(P.du), h->W(T_FCW, l), 4 * C, C, h->w<void>(P.dh));
+    if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "fc dx"))) return rc;
+    if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_mid[l]), h->w<float>(P.mean2[l]), h->w<float>(P.rstd2[l]),
+                          T_LN2G, l, 1, acc)))
+      return rc;
+    // attention output projection
+    if ((rc = bias_grad(h, dres, 1, C, h->G32(T_PROJB, l), acc))) return rc;
+    if ((rc = weight_grad(h, dres_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), P.split[1], acc, "proj dw")))
+      return rc;
+    g = dx_args(h, dres_op, h->W(T_PROJW, l), C, C, h->w<void>(P.datty));
+    if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "proj dx"))) return rc;
+    // attention
+    {
+      const double pairs = (double)h->B * NH * ((double)h->T * (h->T + 1) / 2);
+      rc = hip_check(h, attn_bwd_dsum(h->st, h->prec, h->w<void>(P.atty[l]), h->w<void>(P.datty), h->w<float>(P.dsum),
+                                      h->B, h->T, NH, hd),
+                     "attn dsum");
+      if (rc) return rc;
+      {
+        Timer t(h, K_ATTN_DKV, 4.0 * hd * pairs);
+        rc = hip_check(h, attn_bwd_dkv(h->st, h->prec, h->w<void>(P.qkv[l]), h->w<void>(P.datty), h->w<float>(P.lse[l]),
+                                       h->w<float>(P.dsum), h->w<void>(P.dqkv), h->B, h->T, NH, hd),
+                       "attn dkv");
+      }
+      if (rc) return rc;
+      {
+        Timer t(h, K_ATTN_DQ, 4.0 * hd * pairs);
+        rc = hip_check(h, attn_bwd_dq(h->st, h->prec, h->w<void>(P.qkv[l]), h->w<void>(P.datty), h->w<float>(P.lse[l]),
+                                      h->w<float>(P.dsum), h->w<void>(P.dqkv), h->B, h->T, NH, hd),
+                       "attn dq");
+      }
+      if (rc) return rc;
+    }
+    // qkv projection
+    if ((rc = bias_grad(h, h->w<void>(P.dqkv), 0, 3 * C, h->G32(T_QKVB, l), acc))) return rc;
+    if ((rc = weight_grad(h, h->w<void>(P.dqkv), h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l), P.split[0], acc,
+                          "qkv dw")))
+      return rc;
+    g = dx_args(h, h->w<void>(P.dqkv), h->W(T_QKVW, l), 3 * C, C, h->w<void>(P.dh));
+    if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "qkv dx"))) return rc;
+    if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[l]), h->w<float>(P.mean1[l]), h->w<float>(P.rstd1[l]),
+                          T_LN1G, l, 1, acc)))
+      return rc;
+  }
+  // embeddings: position rows and the (tied) token rows, in a fixed order
+  rc = hip_check(h, embed_bwd(h->st, dres, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva), h->w<int32_t>(P.seg),
+                              h->w<int32_t>(P.nseg), h->G32(T_WTE), h->G32(T_WPE), h->w<float>(P.piece), h->B, h->T,
+                              c.max_seq_len, C, c.vocab_size, acc),
+                 "embed_bwd");
+  return rc;
+}
+
+int gpt2_adamw_step(gpt2_t* h, int step, float lr, float beta1, float beta2, float eps, float weight_decay,
+                    float grad_clip, float* d_grad_norm) {
+  if (!h) return GPT2_ERR_ARG;
+  if (step < 1) return fail(h, GPT2_ERR_ARG, "step must be >= 1");
+  const Plan& P = h->plan;
+  int* flags = h->w<int>(P.flags);
+  float* scale = h->w<float>(P.scale);
+  float* norm = d_grad_norm ? d_grad_norm : h->w<float>(P.norm);
+  int rc = hip_check(h, grad_norm(h->st, h->grads, h->lay.total, h->w<double>(P.normpart), grad_clip, norm, scale, flags),
+                     "grad_norm");
+  if (rc) return rc;
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)step);
+  const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
+  Timer t(h, K_ADAMW, 0);
+  rc = hip_check(h, adamw(h->st, h->params, h->grads, h->m, h->v, h->params_lp, h->lay.total, h->lay.n_decay, lr, beta1,
+                          beta2, eps, weight_decay, (float)bc1, (float)bc2, scale, flags),
+                 "adamw");
+  return rc;
+}
+
+int gpt2_sync_status(gpt2_t* h) {
+  if (!h) return GPT2_ERR_ARG;
+  int rc = hip_check(h, hipStreamSynchronize(h->st), "sync");
+  if (rc) return rc;
+  int f[4] = {0, 0, 0, 0};
+  int* flags = h->w<int>(h->plan.flags);
+  rc = hip_check(h, hipMemcpy(f, flags, sizeof(f), hipMemcpyDeviceToHost), "read flags");
+  if (rc) return rc;
+  const int zero[2] = {0, 0};
+  rc = hip_check(h, hipMemcpy(flags, zero, sizeof(zero), hipMemcpyHostToDevice), "clear flags");
+  if (rc) return rc;
+  if (f[0]) return fail(h, GPT2_ERR_TOKEN_RANGE, "token id or target outside [0, vocab_size)");
+  if (f[1]) return fail(h, GPT2_ERR_NONFINITE, "non-finite gradient norm; the update was skipped");
+  return GPT2_OK;
+}
+
+const char* gpt2_last_error(gpt2_t* h) { return h ? h->err.c_str() : "null handle"; }
+
+const char* gpt2_strerror(int code) {
+  switch (code) {
+    case GPT2_OK: return "ok";
+    case GPT2_ERR_CONFIG: return "invalid model configuration";
+    case GPT2_ERR_SHAPE: return "invalid batch shape";
+    case GPT2_ERR_ARG: return "invalid argument";
+    case GPT2_ERR_HIP: return "HIP runtime error";
+    case GPT2_ERR_TOKEN_RANGE: return "token id or target out of range";
+    case GPT2_ERR_NONFINITE: return "non-finite gradient norm";
+    case GPT2_ERR_WORKSPACE: return "workspace too small";
+    default: return "unknown error";
+  }
+}
+
+int gpt2_kernel_count(void) { return K_COUNT; }
+
+const char* gpt2_kernel_name(int id) { return id >= 0 && id < K_COUNT ? kKernelNames[id] : nullptr; }
+
+int gpt2_timing_enable(gpt2_t* h, int kernel_id, int enable) {
+  if (!h || kernel_id < 0 || kernel_id >= K_COUNT) return GPT2_ERR_ARG;
+  h->timed = enable ? kernel_id : -1;
+  return GPT2_OK;
+}
+
+int gpt2_timing_read(gpt2_t* h, double* total_ms, int64_t* launches, double* flops) {
+  if (!h) return GPT2_ERR_ARG;
+  int rc = hip_check(h, hipStreamSynchronize(h->st), "sync");
+  if (rc) return rc;
+  double ms = 0, fl = 0;
+  for (auto& t : h->timings) {
+    float e = 0;
+    (void)hipEventElapsedTime(&e, t.a, t.b);
+    ms += e;
+    fl += t.flops;
+    (void)hipEventDestroy(t.a);
+    (void)hipEventDestroy(t.b);
+  }
+  if (total_ms) *total_ms = ms;
+  if (launches) *launches = (int64_t)h->timings.size();
+  if (flops) *flops = fl;
+  h->timings.clear();
+  return GPT2_OK;
+}
+
+}  // extern "C"

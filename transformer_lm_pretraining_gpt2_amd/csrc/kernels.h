@@ -1,0 +1,95 @@
+// kernels.h -- host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gpt2k {
+
+enum Prec { F32 = 0, BF16 = 1 };
+
+// ---- matmul: out[i][j] = sum_r A(i, r) * B(j, r), i < M, j < N, r < K ------
+// A(i, r) = A[i*lda + r] (a_t = 0) or A[r*lda + i] (a_t = 1); same for B.
+enum Epi {
+  EPI_STORE = 0,    // out (act type) = acc + bias[j]
+  EPI_GELU = 1,     // aux = acc + bias[j]; out = gelu_tanh(aux)           (act type)
+  EPI_RESID = 2,    // out (fp32) = resid (fp32) + acc + bias[j]
+  EPI_GELU_BWD = 3, // out (act type) = acc * gelu_tanh'(aux)
+  EPI_F32 = 4       // out (fp32) = (accumulate ? out : 0) + acc; split s writes out + s*split_stride
+};
+
+struct GemmArgs {
+  const void* A = nullptr;
+  int64_t lda = 0;
+  const void* B = nullptr;
+  int64_t ldb = 0;
+  int M = 0, N = 0, K = 0;
+  void* C = nullptr;
+  int64_t ldc = 0;
+  const float* bias = nullptr;
+  const float* resid = nullptr;
+  int64_t ldr = 0;
+  void* aux = nullptr;
+  int64_t ldaux = 0;
+  int accumulate = 0;
+  int splits = 1;
+  int64_t split_stride = 0;
+  float alpha = 1.f;  // EPI_STORE / EPI_F32: acc is scaled by alpha before the bias / accumulation
+};
+
+hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArgs& g);
+
+// ---- attention (causal, packed qkv [B*T, 3C]: q heads | k heads | v heads) ----
+hipError_t attn_fwd(hipStream_t st, Prec p, const void* qkv, void* out, float* lse, int B, int T, int NH, int hd);
+// backward in three launches: D = rowsum(dout * out); dK,dV; dQ
+hipError_t attn_bwd_dsum(hipStream_t st, Prec p, const void* out, const void* dout, float* dsum, int B, int T, int NH,
+                         int hd);
+hipError_t attn_bwd_dkv(hipStream_t st, Prec p, const void* qkv, const void* dout, const float* lse, const float* dsum,
+                        void* dqkv, int B, int T, int NH, int hd);
+hipError_t attn_bwd_dq(hipStream_t st, Prec p, const void* qkv, const void* dout, const float* lse, const float* dsum,
+                       void* dqkv, int B, int T, int NH, int hd);
+
+// ---- LayerNorm ----
+hipError_t layernorm_fwd(hipStream_t st, Prec p, const float* x, const float* g, const float* b, void* y, float* mean,
+                         float* rstd, int M, int C);
+// dres (+)= LN backward(dy); also writes dres_lp (act-type copy of dres) when p == BF16,
+// and per-block partials of dgamma/dbeta into part [nblk][2C].
+hipError_t layernorm_bwd(hipStream_t st, Prec p, const void* dy, const float* x, const float* mean, const float* rstd,
+                         const float* g, float* dres, void* dres_lp, int accumulate, float* part, int M, int C,
+                         int* nparts);
+int layernorm_bwd_parts(int M);
+
+// out[j] = (accumulate ? out[j] : 0) + sum_p part[p*ld + j]  (fixed order over p)
+hipError_t reduce_parts(hipStream_t st, const float* part, int nparts, int64_t ld, float* out, int n, int accumulate);
+
+// per-chunk column sums of X [M, N] (act type or fp32) into part [nchunks][N]
+hipError_t colsum_parts(hipStream_t st, Prec p, int x_is_f32, const void* X, int M, int N, float* part, int nchunks);
+
+// ---- embeddings ----
+hipError_t embed_fwd(hipStream_t st, const int32_t* idx, const int32_t* tgt, const float* wte, const float* wpe,
+                     float* x, int B, int T, int C, int V, int* err_flag);
+// stable sort of ids with their positions; segment starts of equal ids
+hipError_t embed_sort(hipStream_t st, const int32_t* idx, int M, int V, int32_t* keys_a, int32_t* vals_a,
+                      int32_t* keys_b, int32_t* vals_b, int32_t* seg_start, int32_t* nseg);
+// piece: fp32 scratch [B*T, C]
+hipError_t embed_bwd(hipStream_t st, const float* dx, const int32_t* sorted_ids, const int32_t* sorted_pos,
+                     const int32_t* seg_start, const int32_t* nseg, float* dwte, float* dwpe, float* piece, int B,
+                     int T, int Tmax, int C, int V, int accumulate_wpe);
+
+// ---- softmax cross-entropy over the real vocabulary, dlogits in place ----
+hipError_t cross_entropy(hipStream_t st, Prec p, void* logits, const int32_t* tgt, float* row_loss, int M, int V, int Vp,
+                         float dscale, int write_grad);
+hipError_t mean_loss(hipStream_t st, const float* row_loss, int M, float* out);
+
+// ---- optimizer ----
+int grad_norm_parts();
+hipError_t grad_norm(hipStream_t st, const float* g, int64_t n, double* part, float clip, float* norm_out,
+                     float* scale_out, int* err_flag);
+// AdamW over the flat buffer; indices < n_decay take weight decay.  g is
+// multiplied by *scale (clip factor); nothing is written when *skip != 0.
+hipError_t adamw(hipStream_t st, float* p, const float* g, float* m, float* v, void* p_lp, int64_t n, int64_t n_decay,
+                 float lr, float b1, float b2, float eps, float wd, float bc1, float bc2, const float* scale,
+                 const int* skip);
+// bf16 copy of fp32 values
+hipError_t to_bf16(hipStream_t st, const float* src, void* dst, int64_t n);
+
+}  // namespace gpt2k

@@ -1,0 +1,699 @@
+// rowops.hip -- the memory-bound kernels of the GPT-2 step on gfx950:
+// LayerNorm forward/backward, column sums, embeddings (forward gather and a
+// deterministic sorted scatter-add backward), the fused softmax
+// cross-entropy, the global gradient norm and AdamW.
+//
+// Every reduction runs in a fixed order (wave butterflies, then wave partials
+// summed in index order, then block partials summed in index order by a
+// second kernel), so results are bitwise reproducible; no kernel uses
+// floating-point atomics.
+#include "common.h"
+#include "kernels.h"
+
+#include <algorithm>
+
+namespace gpt2k {
+namespace {
+
+constexpr int MAXP = 16;  // float pairs per lane: rows of up to 64*2*16 = 2048 elements
+
+template <typename T> struct Pair;
+template <> struct Pair<bf16> { typedef bf16 __attribute__((ext_vector_type(2))) type; };
+template <> struct Pair<float> { typedef float __attribute__((ext_vector_type(2))) type; };
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// LayerNorm forward: one wave per row; mean and biased variance over C,
+// y = (x - mean) * rstd * g + b, rstd = 1/sqrt(var + 1e-5).
+// Lane l holds elements 2l + 128k, 2l + 128k + 1.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256) ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ g,
+                                                     const float* __restrict__ b, T* __restrict__ y,
+                                                     float* __restrict__ mean, float* __restrict__ rstd, int M, int C) {
+  typedef typename Pair<T>::type P;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int np = C / 128;
+  const float* xr = x + (int64_t)row * C;
+  f32x2 v[MAXP];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < MAXP; k++)
+    if (k < np) {
+      v[k] = *reinterpret_cast<const f32x2*>(xr + 2 * lane + 128 * k);
+      s += v[k][0] + v[k][1];
+    }
+  const float mu = wave_sum(s) / C;
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < MAXP; k++)
+    if (k < np) {
+      const float a = v[k][0] - mu, c = v[k][1] - mu;
+      q += a * a + c * c;
+    }
+  const float rs = 1.f / sqrtf(wave_sum(q) / C + 1e-5f);
+  T* yr = y + (int64_t)row * C;
+#pragma unroll
+  for (int k = 0; k < MAXP; k++)
+    if (k < np) {
+      const int c0 = 2 * lane + 128 * k;
+      const f32x2 gg = *reinterpret_cast<const f32x2*>(g + c0);
+      const f32x2 bb = *reinterpret_cast<const f32x2*>(b + c0);
+      P o;
+      o[0] = from_f<T>((v[k][0] - mu) * rs * gg[0] + bb[0]);
+      o[1] = from_f<T>((v[k][1] - mu) * rs * gg[1] + bb[1]);
+      *reinterpret_cast<P*>(yr + c0) = o;
+    }
+  if (lane == 0) {
+    mean[row] = mu;
+    rstd[row] = rs;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm backward fused with the residual-gradient add.  With
+// xhat = (x - mean) rstd and d = dy g:
+//   dx = rstd (d - mean_c(d) - xhat mean_c(d xhat));  dres = [dres +] dx
+// dgamma = sum_rows dy xhat, dbeta = sum_rows dy: each block writes its
+// partial sums (rows visited in a fixed order) to part[block][0:C | C:2C].
+// ---------------------------------------------------------------------------
+constexpr int LNB_BLOCKS = 512;
+
+template <typename T>
+__global__ void __launch_bounds__(256) ln_bwd_kernel(const T* __restrict__ dy, const float* __restrict__ x,
+                                                     const float* __restrict__ mean, const float* __restrict__ rstd,
+                                                     const float* __restrict__ g, float* __restrict__ dres,
+                                                     T* __restrict__ dres_lp, int accumulate, float* __restrict__ part,
+                                                     int M, int C) {
+  typedef typename Pair<T>::type P;
+  extern __shared__ float sh[];  // [4 waves][2C]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int np = C / 128;
+  f32x2 gg[MAXP], ag[MAXP], ab[MAXP];
+#pragma unroll
+  for (int k = 0; k < MAXP; k++)
+    if (k < np) {
+      gg[k] = *reinterpret_cast<const f32x2*>(g + 2 * lane + 128 * k);
+      ag[k] = f32x2{0.f, 0.f};
+      ab[k] = f32x2{0.f, 0.f};
+    }
+  for (int row = blockIdx.x * 4 + w; row < M; row += gridDim.x * 4) {
+    const float mu = mean[row], rs = rstd[row];
+    const T* dyr = dy + (int64_t)row * C;
+    const float* xr = x + (int64_t)row * C;
+    f32x2 xh[MAXP], d[MAXP];
+    float sd = 0.f, sdx = 0.f;
+#pragma unroll
+    for (int k = 0; k < MAXP; k++)
+      if (k < np) {
+        const int c0 = 2 * lane + 128 * k;
+        const P dv = *reinterpret_cast<const P*>(dyr + c0);
+        const f32x2 xv = *reinterpret_cast<const f32x2*>(xr + c0);
+        const float d0 = to_f<T>(dv[0]), d1 = to_f<T>(dv[1]);
+        xh[k] = f32x2{(xv[0] - mu) * rs, (xv[1] - mu) * rs};
+        ag[k][0] += d0 * xh[k][0];
+        ag[k][1] += d1 * xh[k][1];
+        ab[k][0] += d0;
+        ab[k][1] += d1;
+        d[k] = f32x2{d0 * gg[k][0], d1 * gg[k][1]};
+        sd += d[k][0] + d[k][1];
+        sdx += d[k][0] * xh[k][0] + d[k][1] * xh[k][1];
+      }
+    sd = wave_sum(sd) / C;
+    sdx = wave_sum(sdx) / C;
+    float* rr = dres + (int64_t)row * C;
+#pragma unroll
+    for (int k = 0; k < MAXP; k++)
+      if (k < np) {
+        const int c0 = 2 * lane + 128 * k;
+        f32x2 o{rs * (d[k][0] - sd - xh[k][0] * sdx), rs * (d[k][1] - sd - xh[k][1] * sdx)};
+        if (accumulate) {
+          const f32x2 prev = *reinterpret_cast<const f32x2*>(rr + c0);
+          o[0] += prev[0];
+          o[1] += prev[1];
+        }
+        *reinterpret_cast<f32x2*>(rr + c0) = o;
+        if (dres_lp) {
+          P lp;
+          lp[0] = from_f<T>(o[0]);
+          lp[1] = from_f<T>(o[1]);
+          *reinterpret_cast<P*>(dres_lp + (int64_t)row * C + c0) = lp;
+        }
+      }
+  }
+  // block partials: waves combined in index order
+#pragma unroll
+  for (int k = 0; k < MAXP; k++)
+    if (k < np) {
+      const int c0 = 2 * lane + 128 * k;
+      sh[w * 2 * C + c0] = ag[k][0];
+      sh[w * 2 * C + c0 + 1] = ag[k][1];
+      sh[w * 2 * C + C + c0] = ab[k][0];
+      sh[w * 2 * C + C + c0 + 1] = ab[k][1];
+    }
+  __syncthreads();
+  for (int j = threadIdx.x; j < 2 * C; j += 256)
+    part[(int64_t)blockIdx.x * 2 * C + j] = ((sh[j] + sh[2 * C + j]) + sh[4 * C + j]) + sh[6 * C + j];
+}
+
+// out[j] = [out[j] +] sum_p part[p*ld + j], p in index order
+__global__ void reduce_parts_kernel(const float* __restrict__ part, int nparts, int64_t ld, float* __restrict__ out,
+                                    int n, int accumulate) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= n) return;
+  float s = 0.f;
+  for (int p = 0; p < nparts; p++) s += part[(int64_t)p * ld + j];
+  out[j] = accumulate ? out[j] + s : s;
+}
+
+// part[chunk][j] = sum over rows of the chunk of X[row][j] (rows in order)
+template <typename T>
+__global__ void colsum_kernel(const T* __restrict__ X, int M, int N, float* __restrict__ part, int rows_per_chunk) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= N) return;
+  const int r0 = blockIdx.y * rows_per_chunk, r1 = min(M, r0 + rows_per_chunk);
+  float s = 0.f;
+  for (int r = r0; r < r1; r++) s += to_f<T>(X[(int64_t)r * N + j]);
+  part[(int64_t)blockIdx.y * N + j] = s;
+}
+
+// ---------------------------------------------------------------------------
+// Embedding forward: x[b,t] = wte[id[b,t]] + wpe[t]  (one wave per row).
+// Ids or targets outside [0, V) set *err (the gather then reads row 0).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) embed_fwd_kernel(const int32_t* __restrict__ idx, const int32_t* __restrict__ tgt,
+                                                        const float* __restrict__ wte, const float* __restrict__ wpe,
+                                                        float* __restrict__ x, int M, int T_, int C, int V,
+                                                        int* __restrict__ err) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;
+  int id = idx[row];
+  bool bad = id < 0 || id >= V;
+  if (tgt) {
+    const int tg = tgt[row];
+    bad = bad || tg < 0 || tg >= V;
+  }
+  if (bad) {
+    if (lane == 0) atomicOr(err, 1);
+    if (id < 0 || id >= V) id = 0;
+  }
+  const int t = row % T_;
+  const float* a = wte + (int64_t)id * C;
+  const float* p = wpe + (int64_t)t * C;
+  float* o = x + (int64_t)row * C;
+  for (int c = 2 * lane; c < C; c += 128) {
+    const f32x2 u = *reinterpret_cast<const f32x2*>(a + c);
+    const f32x2 v = *reinterpret_cast<const f32x2*>(p + c);
+    *reinterpret_cast<f32x2*>(o + c) = f32x2{u[0] + v[0], u[1] + v[1]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stable LSD radix sort of (id, position) pairs in one workgroup of 1024
+// threads (8-bit digits), then the start index of every run of equal ids.
+// The result depends only on the ids: positions with equal id stay in
+// increasing order, so every later sum over a run has a fixed order.
+// ---------------------------------------------------------------------------
+constexpr int SORT_T = 1024;
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
+
+__global__ void __launch_bounds__(SORT_T) embed_sort_kernel(const int32_t* __restrict__ idx, int M, int passes,
+                                                            int32_t* ka, int32_t* va, int32_t* kb, int32_t* vb,
+                                                            int32_t* __restrict__ seg_start, int32_t* __restrict__ nseg) {
+  __shared__ int hist[256];
+  __shared__ int base[256];
+  __shared__ int wcnt[SORT_T / 64][257];
+  __shared__ int wtot[SORT_T / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int32_t* kin = idx;
+  const int32_t* vin = nullptr;
+  int32_t *kout = ka, *vout = va;
+  for (int pass = 0; pass < passes; pass++) {
+    const int shift = 8 * pass;
+    if (tid < 256) {
+      hist[tid] = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < M; i += SORT_T) atomicAdd(&hist[(kin[i] >> shift) & 255], 1);
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int d = 0; d < 256; d++) {
+        base[d] = run;
+        run += hist[d];
+      }
+    }
+    __syncthreads();
+    for (int t0 = 0; t0 < M; t0 += SORT_T) {
+      const int i = t0 + tid;
+      const bool valid = i < M;
+      const int key = valid ? kin[i] : 0;
+      const int val = valid ? (vin ? vin[i] : i) : 0;
+      const int d = (key >> shift) & 255;
+      uint64_t mask = __ballot(valid);
+#pragma unroll
+      for (int bit = 0; bit < 8; bit++) {
+        const uint64_t bb = __ballot((d >> bit) & 1);
+        mask &= ((d >> bit) & 1) ? bb : ~bb;
+      }
+      const int rank = __popcll(mask & lanemask_lt(lane));
+      for (int j = tid; j < (SORT_T / 64) * 257; j += SORT_T) (&wcnt[0][0])[j] = 0;
+      __syncthreads();
+      if (valid && rank == 0) wcnt[w][d] = __popcll(mask);
+      __syncthreads();
+      if (valid) {
+        int off = base[d] + rank;
+        for (int ww = 0; ww < w; ww++) off += wcnt[ww][d];
+        kout[off] = key;
+        vout[off] = val;
+      }
+      __syncthreads();
+      if (tid < 256) {
+        int add = 0;
+        for (int ww = 0; ww < SORT_T / 64; ww++) add += wcnt[ww][tid];
+        base[tid] += add;
+      }
+      __syncthreads();
+    }
+    // next pass reads what this one wrote
+    __threadfence_block();
+    kin = kout;
+    vin = vout;
+    kout = (kout == ka) ? kb : ka;
+    vout = (vout == va) ? vb : va;
+    __syncthreads();
+  }
+  // kin/vin hold the sorted result; make sure it sits in (ka, va)
+  if (kin != ka) {
+    for (int i = tid; i < M; i += SORT_T) {
+      ka[i] = kin[i];
+      va[i] = vin[i];
+    }
+    __syncthreads();
+  }
+  // run starts: flag[i] = (i == 0 || key[i] != key[i-1]); exclusive scan of flags
+  int running = 0;
+  for (int t0 = 0; t0 < M; t0 += SORT_T) {
+    const int i = t0 + tid;
+    const bool f = i < M && (i == 0 || ka[i] != ka[i - 1]);
+    const uint64_t bal = __ballot(f);
+    const int wr = __popcll(bal & lanemask_lt(lane));
+    if (lane == 0) wtot[w] = __popcll(bal);
+    __syncthreads();
+    int off = running + wr;
+    for (int ww = 0; ww < w; ww++) off += wtot[ww];
+    if (f) seg_start[off] = i;
+    int tot = 0;
+    for (int ww = 0; ww < SORT_T / 64; ww++) tot += wtot[ww];
+    running += tot;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    seg_start[running] = M;
+    *nseg = running;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Embedding backward.
+// dwpe[t] = [dwpe[t] +] sum_b dx[b, t]  (b in order; rows t >= T are zeroed
+// when not accumulating).  dwte[id] += sum over the positions with that id,
+// in sorted (= increasing position) order, computed in two steps so a very
+// frequent id does not serialise: pieces of at most EMB_P sorted positions
+// are summed in parallel, then each run adds up its pieces in order.
+// ---------------------------------------------------------------------------
+constexpr int EMB_P = 64;
+
+__global__ void dwpe_kernel(const float* __restrict__ dx, float* __restrict__ dwpe, int B, int T_, int Tmax, int C,
+                            int accumulate) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)Tmax * C) return;
+  const int t = e / C, c = e % C;
+  float s = 0.f;
+  if (t < T_)
+    for (int b = 0; b < B; b++) s += dx[((int64_t)b * T_ + t) * C + c];
+  dwpe[e] = accumulate ? dwpe[e] + s : s;
+}
+
+// grid (ceil(M/EMB_P), C/64), one wave: lane = channel within a 64-wide slice.
+__global__ void __launch_bounds__(64) dwte_piece_kernel(const float* __restrict__ dx, const int32_t* __restrict__ skey,
+                                                        const int32_t* __restrict__ spos, float* __restrict__ piece,
+                                                        int M, int C) {
+  const int c = blockIdx.y * 64 + threadIdx.x;
+  const int i0 = blockIdx.x * EMB_P, i1 = min(M, i0 + EMB_P);
+  float acc = 0.f;
+  int start = i0;
+  for (int i = i0; i < i1; i++) {
+    if (i > start && skey[i] != skey[i - 1]) {
+      piece[(int64_t)start * C + c] = acc;
+      acc = 0.f;
+      start = i;
+    }
+    acc += dx[(int64_t)spos[i] * C + c];
+  }
+  if (i1 > i0) piece[(int64_t)start * C + c] = acc;
+}
+
+// grid (G, C/64), one wave: runs s = blockIdx.x, blockIdx.x + G, ...
+__global__ void __launch_bounds__(64) dwte_run_kernel(const float* __restrict__ piece, const int32_t* __restrict__ skey,
+                                                      const int32_t* __restrict__ seg_start,
+                                                      const int32_t* __restrict__ nseg, float* __restrict__ dwte, int C,
+                                                      int V) {
+  const int c = blockIdx.y * 64 + threadIdx.x;
+  const int ns = *nseg;
+  for (int s = blockIdx.x; s < ns; s += gridDim.x) {
+    const int a = seg_start[s], e = seg_start[s + 1];
+    float acc = piece[(int64_t)a * C + c];
+    for (int p = (a / EMB_P + 1) * EMB_P; p < e; p += EMB_P) acc += piece[(int64_t)p * C + c];
+    const int id = skey[a];
+    if (id >= 0 && id < V) dwte[(int64_t)id * C + c] += acc;  // bad ids were flagged in the forward pass
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused softmax cross-entropy, one block (1024 threads) per row.  The row is
+// read once into registers; max and sum of exp run over the real vocabulary
+// [0, V); loss = logsumexp - z[target]; the logits are overwritten in place
+// with dscale * (softmax - onehot) on [0, V) and 0 on the padded columns.
+// Probabilities are never stored.
+// ---------------------------------------------------------------------------
+constexpr int CE_T = 1024;
+
+template <typename T, int NV>
+__global__ void __launch_bounds__(CE_T) ce_kernel(T* __restrict__ logits, const int32_t* __restrict__ tgt,
+                                                  float* __restrict__ row_loss, int V, int Vp, float dscale,
+                                                  int write_grad) {
+  typedef typename Frag<T>::type F;
+  __shared__ float red[CE_T / 64];
+  __shared__ float zt;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t row = blockIdx.x;
+  T* z = logits + row * Vp;
+  const int nvec = Vp / 8;
+  const int y = min(max(tgt[row], 0), V - 1);  // out-of-range targets were flagged by the embedding pass
+  if (tid == 0) zt = to_f<T>(z[y]);
+  F v[NV];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < NV; k++) {
+    const int vi = tid + k * CE_T;
+    if (vi < nvec) {
+      v[k] = ld8(z + vi * 8);
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        if (vi * 8 + e < V) mx = fmaxf(mx, to_f<T>(v[k][e]));
+    }
+  }
+  mx = wave_max(mx);
+  if (lane == 0) red[w] = mx;
+  __syncthreads();
+  mx = red[0];
+#pragma unroll
+  for (int i = 1; i < CE_T / 64; i++) mx = fmaxf(mx, red[i]);
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; k++) {
+    const int vi = tid + k * CE_T;
+    if (vi < nvec)
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        if (vi * 8 + e < V) s += __expf(to_f<T>(v[k][e]) - mx);
+  }
+  s = wave_sum(s);
+  if (lane == 0) red[w] = s;
+  __syncthreads();
+  s = red[0];
+#pragma unroll
+  for (int i = 1; i < CE_T / 64; i++) s += red[i];
+  const float lse = mx + __logf(s);
+  if (tid == 0) row_loss[row] = lse - zt;
+  if (!write_grad) return;
+#pragma unroll
+  for (int k = 0; k < NV; k++) {
+    const int vi = tid + k * CE_T;
+    if (vi < nvec) {
+      F o;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const int j = vi * 8 + e;
+        const float g = j < V ? (__expf(to_f<T>(v[k][e]) - lse) - (j == y ? 1.f : 0.f)) * dscale : 0.f;
+        o[e] = from_f<T>(g);
+      }
+      st8(z + vi * 8, o);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(1024) mean_loss_kernel(const float* __restrict__ row_loss, int M,
+                                                         float* __restrict__ out) {
+  __shared__ double red[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  double s = 0.0;
+  for (int i = tid; i < M; i += 1024) s += row_loss[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (lane == 0) red[w] = s;
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+    for (int i = 0; i < 16; i++) t += red[i];
+    *out = (float)(t / M);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Global gradient norm: block b sums g^2 over its contiguous chunk (fixed
+// order), then one block adds the partials in order and derives the clip
+// factor min(1, clip / norm); a non-finite norm sets the error and skip flags.
+// ---------------------------------------------------------------------------
+constexpr int NORM_BLOCKS = 1024;
+
+__global__ void __launch_bounds__(256) norm_part_kernel(const float* __restrict__ g, int64_t n,
+                                                        double* __restrict__ part) {
+  __shared__ double red[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int64_t nq = n / 4;
+  const int64_t per = (nq + gridDim.x - 1) / gridDim.x;
+  const int64_t q0 = blockIdx.x * per, q1 = min(nq, q0 + per);
+  double s = 0.0;
+  for (int64_t q = q0 + tid; q < q1; q += 256) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(g + 4 * q);
+    s += (double)v[0] * v[0] + (double)v[1] * v[1] + (double)v[2] * v[2] + (double)v[3] * v[3];
+  }
+  if (blockIdx.x == gridDim.x - 1)
+    for (int64_t i = 4 * nq + tid; i < n; i += 256) s += (double)g[i] * g[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (lane == 0) red[w] = s;
+  __syncthreads();
+  if (tid == 0) part[blockIdx.x] = ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+__global__ void __launch_bounds__(256) norm_final_kernel(const double* __restrict__ part, int nparts, float clip,
+                                                         float* __restrict__ norm_out, float* __restrict__ scale_out,
+                                                         int* __restrict__ flags) {
+  __shared__ double red[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  double s = 0.0;
+  for (int i = tid; i < nparts; i += 256) s += part[i];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+  if (lane == 0) red[w] = s;
+  __syncthreads();
+  if (tid == 0) {
+    const double tot = ((red[0] + red[1]) + red[2]) + red[3];
+    const float nrm = (float)sqrt(tot);
+    if (norm_out) *norm_out = nrm;
+    const bool finite = isfinite(nrm);
+    *scale_out = finite && nrm > clip ? clip / nrm : 1.f;
+    flags[2] = finite ? 0 : 1;  // skip this update
+    if (!finite) flags[1] = 1;  // reported by the next status check
+  }
+}
+
+// AdamW with bias correction and decoupled weight decay on indices < n_decay.
+__global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
+                                                    float* __restrict__ m, float* __restrict__ v,
+                                                    bf16* __restrict__ p_lp, int64_t nq, int64_t n_decay, float lr,
+                                                    float b1, float b2, float eps, float wd, float rbc1, float rbc2,
+                                                    const float* __restrict__ scale, const int* __restrict__ flags) {
+  if (flags[2]) return;
+  const float sc = *scale;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = 4 * q;
+    f32x4 pp = *reinterpret_cast<const f32x4*>(p + i);
+    const f32x4 gg = *reinterpret_cast<const f32x4*>(g + i);
+    f32x4 mm = *reinterpret_cast<const f32x4*>(m + i);
+    f32x4 vv = *reinterpret_cast<const f32x4*>(v + i);
+    const float d = i < n_decay ? wd : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const float gr = gg[e] * sc;
+      mm[e] = b1 * mm[e] + (1.f - b1) * gr;
+      vv[e] = b2 * vv[e] + (1.f - b2) * gr * gr;
+      const float mh = mm[e] * rbc1, vh = vv[e] * rbc2;
+      pp[e] -= lr * (mh / (sqrtf(vh) + eps) + d * pp[e]);
+    }
+    *reinterpret_cast<f32x4*>(p + i) = pp;
+    *reinterpret_cast<f32x4*>(m + i) = mm;
+    *reinterpret_cast<f32x4*>(v + i) = vv;
+    if (p_lp) {
+      bf16x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; e++) o[e] = (bf16)pp[e];
+      *reinterpret_cast<bf16x4*>(p_lp + i) = o;
+    }
+  }
+}
+
+__global__ void to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = (bf16)src[i];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t layernorm_fwd(hipStream_t st, Prec p, const float* x, const float* g, const float* b, void* y, float* mean,
+                         float* rstd, int M, int C) {
+  if (C % 128 != 0 || C > 128 * MAXP) return hipErrorInvalidValue;
+  dim3 grid((M + 3) / 4);
+  if (p == BF16)
+    hipLaunchKernelGGL(ln_fwd_kernel<bf16>, grid, dim3(256), 0, st, x, g, b, static_cast<bf16*>(y), mean, rstd, M, C);
+  else
+    hipLaunchKernelGGL(ln_fwd_kernel<float>, grid, dim3(256), 0, st, x, g, b, static_cast<float*>(y), mean, rstd, M, C);
+  return hipGetLastError();
+}
+
+int layernorm_bwd_parts(int M) { return std::min(LNB_BLOCKS, (M + 3) / 4); }
+
+hipError_t layernorm_bwd(hipStream_t st, Prec p, const void* dy, const float* x, const float* mean, const float* rstd,
+                         const float* g, float* dres, void* dres_lp, int accumulate, float* part, int M, int C,
+                         int* nparts) {
+  if (C % 128 != 0 || C > 128 * MAXP) return hipErrorInvalidValue;
+  const int nb = layernorm_bwd_parts(M);
+  *nparts = nb;
+  const size_t shm = 4 * 2 * C * sizeof(float);
+  if (p == BF16)
+    hipLaunchKernelGGL(ln_bwd_kernel<bf16>, dim3(nb), dim3(256), shm, st, static_cast<const bf16*>(dy), x, mean, rstd, g,
+                       dres, static_cast<bf16*>(dres_lp), accumulate, part, M, C);
+  else
+    hipLaunchKernelGGL(ln_bwd_kernel<float>, dim3(nb), dim3(256), shm, st, static_cast<const float*>(dy), x, mean, rstd,
+                       g, dres, static_cast<float*>(dres_lp), accumulate, part, M, C);
+  return hipGetLastError();
+}
+
+hipError_t reduce_parts(hipStream_t st, const float* part, int nparts, int64_t ld, float* out, int n, int accumulate) {
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3((n + 255) / 256), dim3(256), 0, st, part, nparts, ld, out, n, accumulate);
+  return hipGetLastError();
+}
+
+hipError_t colsum_parts(hipStream_t st, Prec p, int x_is_f32, const void* X, int M, int N, float* part, int nchunks) {
+  const int rpc = (M + nchunks - 1) / nchunks;
+  dim3 grid((N + 255) / 256, nchunks);
+  if (x_is_f32 || p == F32)
+    hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(X), M, N, part, rpc);
+  else
+    hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(256), 0, st, static_cast<const bf16*>(X), M, N, part, rpc);
+  return hipGetLastError();
+}
+
+hipError_t embed_fwd(hipStream_t st, const int32_t* idx, const int32_t* tgt, const float* wte, const float* wpe,
+                     float* x, int B, int T_, int C, int V, int* err_flag) {
+  const int M = B * T_;
+  hipLaunchKernelGGL(embed_fwd_kernel, dim3((M + 3) / 4), dim3(256), 0, st, idx, tgt, wte, wpe, x, M, T_, C, V,
+                     err_flag);
+  return hipGetLastError();
+}
+
+hipError_t embed_sort(hipStream_t st, const int32_t* idx, int M, int V, int32_t* keys_a, int32_t* vals_a,
+                      int32_t* keys_b, int32_t* vals_b, int32_t* seg_start, int32_t* nseg) {
+  int passes = 1;
+  while (passes < 4 && (int64_t)(V - 1) >> (8 * passes)) passes++;
+  hipLaunchKernelGGL(embed_sort_kernel, dim3(1), dim3(SORT_T), 0, st, idx, M, passes, keys_a, vals_a, keys_b, vals_b,
+                     seg_start, nseg);
+  return hipGetLastError();
+}
+
+hipError_t embed_bwd(hipStream_t st, const float* dx, const int32_t* sorted_ids, const int32_t* sorted_pos,
+                     const int32_t* seg_start, const int32_t* nseg, float* dwte, float* dwpe, float* piece, int B,
+                     int T_, int Tmax, int C, int V, int accumulate_wpe) {
+  const int M = B * T_;
+  const int64_t nw = (int64_t)Tmax * C;
+  hipLaunchKernelGGL(dwpe_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, st, dx, dwpe, B, T_, Tmax, C,
+                     accumulate_wpe);
+  hipLaunchKernelGGL(dwte_piece_kernel, dim3((M + EMB_P - 1) / EMB_P, C / 64), dim3(64), 0, st, dx, sorted_ids,
+                     sorted_pos, piece, M, C);
+  hipLaunchKernelGGL(dwte_run_kernel, dim3(std::min(M, 2048), C / 64), dim3(64), 0, st, piece, sorted_ids, seg_start,
+                     nseg, dwte, C, V);
+  return hipGetLastError();
+}
+
+hipError_t cross_entropy(hipStream_t st, Prec p, void* logits, const int32_t* tgt, float* row_loss, int M, int V, int Vp,
+                         float dscale, int write_grad) {
+  if (Vp % 8 != 0) return hipErrorInvalidValue;
+  const int nvec = Vp / 8;
+  const int nv = (nvec + CE_T - 1) / CE_T;
+#define CE_LAUNCH(TT, NV)                                                                                            \
+  hipLaunchKernelGGL((ce_kernel<TT, NV>), dim3(M), dim3(CE_T), 0, st, static_cast<TT*>(logits), tgt, row_loss, V, Vp, \
+                     dscale, write_grad)
+#define CE_DISPATCH(TT)     \
+  if (nv <= 1)              \
+    CE_LAUNCH(TT, 1);       \
+  else if (nv <= 2)         \
+    CE_LAUNCH(TT, 2);       \
+  else if (nv <= 4)         \
+    CE_LAUNCH(TT, 4);       \
+  else if (nv <= 8)         \
+    CE_LAUNCH(TT, 8);       \
+  else                      \
+    return hipErrorInvalidValue;
+  if (p == BF16) {
+    CE_DISPATCH(bf16)
+  } else {
+    CE_DISPATCH(float)
+  }
+#undef CE_DISPATCH
+#undef CE_LAUNCH
+  return hipGetLastError();
+}
+
+hipError_t mean_loss(hipStream_t st, const float* row_loss, int M, float* out) {
+  hipLaunchKernelGGL(mean_loss_kernel, dim3(1), dim3(1024), 0, st, row_loss, M, out);
+  return hipGetLastError();
+}
+
+int grad_norm_parts() { return NORM_BLOCKS; }
+
+hipError_t grad_norm(hipStream_t st, const float* g, int64_t n, double* part, float clip, float* norm_out,
+                     float* scale_out, int* flags) {
+  hipLaunchKernelGGL(norm_part_kernel, dim3(NORM_BLOCKS), dim3(256), 0, st, g, n, part);
+  hipLaunchKernelGGL(norm_final_kernel, dim3(1), dim3(256), 0, st, part, NORM_BLOCKS, clip, norm_out, scale_out, flags);
+  return hipGetLastError();
+}
+
+hipError_t adamw(hipStream_t st, float* p, const float* g, float* m, float* v, void* p_lp, int64_t n, int64_t n_decay,
+                 float lr, float b1, float b2, float eps, float wd, float bc1, float bc2, const float* scale,
+                 const int* flags) {
+  if (n % 4 != 0 || n_decay % 4 != 0) return hipErrorInvalidValue;
+  const int64_t nq = n / 4;
+  const unsigned blocks = (unsigned)std::min<int64_t>((nq + 255) / 256, 8192);
+  hipLaunchKernelGGL(adamw_kernel, dim3(blocks), dim3(256), 0, st, p, g, m, v, static_cast<bf16*>(p_lp), nq, n_decay, lr,
+                     b1, b2, eps, wd, 1.f / bc1, 1.f / bc2, scale, flags);
+  return hipGetLastError();
+}
+
+hipError_t to_bf16(hipStream_t st, const float* src, void* dst, int64_t n) {
+  const unsigned blocks = (unsigned)std::min<int64_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(blocks), dim3(256), 0, st, src, static_cast<bf16*>(dst), n);
+  return hipGetLastError();
+}
+
+}  // namespace gpt2k
