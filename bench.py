@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Throughput of one GPT-2 training step on one MI355X.
+
+A step is the whole path: K micro-steps of forward + backward (token and
+position embedding, pre-LN attention/GELU blocks, tied head, fused
+cross-entropy, and their gradients) followed by global-norm clipping and
+AdamW, all in the HIP library.  Inputs are synthetic Zipf(s=1) token streams
+already resident in device memory; weights are a random GPT-2 init.
+
+Prints one JSON line: tokens/s (whole job), MFU against the bf16 dense MFMA
+peak, the roofline of the dominant kernel measured with HIP events on the
+library's stream during the timed steps, and the CPU oracle's throughput on a
+bounded sample of the same workload.
+
+Only one GPU is supported; --gpus > 1 exits with a message.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "training tokens/sec + MFU, GPT-2 124M bf16 B=16 T=1024, 1×MI355X"
+# Per-kernel roofline: which kernel dominates the step (from the rocprofv3
+# kernel-trace summary under profiles/) and how it is bounded.
+DOMINANT = {"gpt2_124m": "gemm_tn_f32"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "transformer_lm_pretraining_gpt2_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
+    when they are missing or were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = d.get(workload, {}).get(kernel)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(model, seed_stream, sample_tokens):
+    """The oracle (plain fp32 C++, not tuned) on one sample sequence of the
+    same workload: forward, backward, clip and AdamW over all parameters."""
+    import numpy as np
+
+    from oracle import oracle
+    from transformer_lm_pretraining_gpt2_amd import synth
+
+    T = sample_tokens
+    lay = oracle.param_layout(model)
+    p = synth.init_params(lay, model.n_layer, model.vocab_size)
+    ids, tgt = synth.micro_batch(seed_stream, 1, T, 0)
+    g = np.zeros_like(p)
+    m = np.zeros_like(p)
+    v = np.zeros_like(p)
+    t0 = time.perf_counter()
+    oracle.fwd_bwd(model, 1, T, p, ids, tgt, 1.0, g, R=np.float32)
+    oracle.clip_grads(g, 1.0, R=np.float32)
+    oracle.adamw(model, p, g, m, v, 1, 6e-4, R=np.float32)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or os.cpu_count()
+    return {"value": T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"one {T}-token sequence of the same model (B=1): fp32 forward+backward, clip and AdamW over all "
+                      f"{oracle.num_params(model)} parameters, {dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="gpt2_124m")
+    ap.add_argument("--precision", default=None, help="fp32 or bf16 (default: the workload's)")
+    ap.add_argument("--roofline-kernel", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(data parallelism is a design note only).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from transformer_lm_pretraining_gpt2_amd import binding, synth
+    from transformer_lm_pretraining_gpt2_amd.config import CONFIGS, MI355X_BF16_PEAK_FLOPS, MI355X_FP32_MFMA_PEAK_FLOPS
+    from transformer_lm_pretraining_gpt2_amd.config import flops_per_token, lr_at
+
+    rc = CONFIGS[args.config]
+    model = rc.model
+    prec = args.precision or rc.precision
+    B, T, K = rc.B, rc.T, rc.K
+    S, W = args.steps, args.warmup
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    step = binding.TrainStep(model, B, T, prec, device=dev)
+    lay = step.layout
+    step.set_params(synth.init_params(lay, model.n_layer, model.vocab_size))
+    n_tok = synth.stream_length(W + S, K, B, T)
+    stream = synth.zipf_stream(n_tok, model.vocab_size) if rc.data == "zipf" else synth.uniform_stream(
+        n_tok, model.vocab_size)
+    # every micro-batch of the run, resident in HBM before timing starts
+    nmb = (W + S) * K
+    ids_all = np.empty((nmb, B * T), np.int32)
+    tgt_all = np.empty((nmb, B * T), np.int32)
+    for i in range(nmb):
+        a, b = synth.micro_batch(stream, B, T, i)
+        ids_all[i], tgt_all[i] = a.reshape(-1), b.reshape(-1)
+    d_ids = torch.from_numpy(ids_all).to(dev)
+    d_tgt = torch.from_numpy(tgt_all).to(dev)
+    loss = torch.zeros(1, device=dev)
+    norm = torch.zeros(1, device=dev)
+
+    def one_step(s):
+        for k in range(K):
+            i = s * K + k
+            step.forward(d_ids[i], d_tgt[i], loss)
+            step.backward(k, K)
+        step.adamw_step(s + 1, lr_at(s, rc.max_lr, rc.warmup, rc.max_steps), rc.beta1, rc.beta2, rc.eps,
+                        rc.weight_decay, rc.grad_clip, norm)
+
+    for s in range(W):
+        one_step(s)
+    st = step.sync_status()
+    if st != 0:
+        raise SystemExit(f"warmup step failed: {binding.ERRORS.get(st, st)}")
+    first_loss = loss.item()
+
+    kname = args.roofline_kernel or DOMINANT.get(args.config, "gemm_tn_f32")
+    step.timing_enable(kname, True)
+    step.timing_read()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for s in range(W, W + S):
+        one_step(s)
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k_ms, k_launches, k_flops = step.timing_read()
+    step.timing_enable(kname, False)
+    st = step.sync_status()
+    if st != 0:
+        raise SystemExit(f"timed step failed: {binding.ERRORS.get(st, st)}")
+
+    wall_ms = (t1 - t0) * 1000 / S
+    ev_ms = ev0.elapsed_time(ev1) / S
+    ms = max(wall_ms, ev_ms)
+    tokens = K * B * T
+    tps = tokens / (ms / 1000)
+    fpt = flops_per_token(model, T, causal=True)
+    peak = MI355X_BF16_PEAK_FLOPS if prec == "bf16" else MI355X_FP32_MFMA_PEAK_FLOPS
+    mfu = tps * fpt / peak
+
+    roof = None
+    if k_launches:
+        achieved = k_flops / (k_ms / 1000)
+        traffic = measured_traffic(kname, args.config)
+        roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": round(peak / 1e12, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                "avg_launch_us": round(1000 * k_ms / k_launches, 2), "launches_per_step": k_launches / S,
+                "flops_per_launch": k_flops / k_launches}
+
+    out = {
+        "metric": METRIC if args.config == "gpt2_124m" else f"training tokens/sec + MFU, {args.config}",
+        "value": round(tps, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": S,
+        "warmup": W,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "mfu": round(mfu, 4),
+        "tflops": round(tps * fpt / 1e12, 1),
+        "flops_per_token": fpt,
+        "flops_per_token_noncausal": flops_per_token(model, T, causal=False),
+        "dtype": prec,
+        "data": f"synthetic: {'Zipf(s=1.0)' if rc.data == 'zipf' else 'uniform'} token ids over {model.vocab_size}, "
+                f"seed {synth.DATA_SEED}; random GPT-2 init, seed {synth.INIT_SEED}",
+        "config": {"workload": f"{args.config}: one training step (fwd+bwd+clip+AdamW), B={B} T={T} K={K}, "
+                               f"L={model.n_layer} nh={model.n_head} C={model.n_embd} V={model.vocab_size}"
+                               f"->{model.padded_vocab_size}",
+                   "global_batch": B * K, "seq_len": T, "grad_accum": K, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "loss_first_timed": round(first_loss, 4),
+        "loss_last": round(loss.item(), 4),
+        "context": {"a100_pytorch_124m_tok_s": 182000,
+                    "note": "pages' single-A100 figure (PyTorch, bf16, compile, flash attention); context only"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(model, stream, min(args.cpu_sample_tokens, T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -36,36 +36,39 @@ template <typename T> struct V16;
 template <> struct V16<bf16> { typedef bf16x8 type; static constexpr int n = 8; };
 template <> struct V16<float> { typedef f32x4 type; static constexpr int n = 4; };
 
-// Copy a [KT][HD] row tile (rows `ld` apart in global) into LDS [KT][HD+pad].
+// One KT x HD row tile (rows `ld` apart in global memory) held in registers
+// as 8 (rows) x VE (columns) blocks, one block per thread of [t0, t0 + NBLK).
+// It is read from global memory once and can be written to LDS row-major
+// ([KT][HD+pad]) and/or transposed ([HD][KT+pad]); loading the next tile
+// while the current one is consumed hides the memory latency.
 template <typename T, int HD>
-__device__ __forceinline__ void load_rows(T* s, const T* g, int64_t ld, int tid) {
-  constexpr int VE = V16<T>::n, LD = HD + VE, CPR = HD / VE, TOTAL = KT * CPR;
-  for (int idx = tid; idx < TOTAL; idx += NW * 64) {
-    const int r = idx / CPR, c = idx % CPR;
-    *reinterpret_cast<f32x4*>(s + r * LD + c * VE) = *reinterpret_cast<const f32x4*>(g + (int64_t)r * ld + c * VE);
-  }
-}
-
-// Copy a [KT][HD] row tile into LDS transposed: [HD][KT+pad].
-template <typename T, int HD>
-__device__ __forceinline__ void load_rows_t(T* s, const T* g, int64_t ld, int tid) {
+struct BlockTile {
   typedef typename V16<T>::type V;
   typedef typename Frag<T>::type F;
-  constexpr int VE = V16<T>::n, LD = KT + VE, NCB = HD / VE, TOTAL = (KT / 8) * NCB;
-  for (int blk = tid; blk < TOTAL; blk += NW * 64) {
-    const int rb = blk / NCB, cb = blk % NCB;
-    V v[8];
+  static constexpr int VE = V16<T>::n, NCB = HD / VE, NBLK = (KT / 8) * NCB;
+  static constexpr int LDR = HD + VE, LDT = KT + VE;
+  V v[8];
+  __device__ __forceinline__ void load(const T* g, int64_t ld, int i) {
+    const int rb = i / NCB, cb = i % NCB;
 #pragma unroll
     for (int a = 0; a < 8; a++) v[a] = *reinterpret_cast<const V*>(g + (int64_t)(rb * 8 + a) * ld + cb * VE);
+  }
+  __device__ __forceinline__ void store_rows(T* s, int i) const {
+    const int rb = i / NCB, cb = i % NCB;
+#pragma unroll
+    for (int a = 0; a < 8; a++) *reinterpret_cast<V*>(s + (rb * 8 + a) * LDR + cb * VE) = v[a];
+  }
+  __device__ __forceinline__ void store_t(T* s, int i) const {
+    const int rb = i / NCB, cb = i % NCB;
 #pragma unroll
     for (int b = 0; b < VE; b++) {
       F w;
 #pragma unroll
       for (int a = 0; a < 8; a++) w[a] = v[a][b];
-      st8(s + (cb * VE + b) * LD + rb * 8, w);
+      st8(s + (cb * VE + b) * LDT + rb * 8, w);
     }
   }
-}
+};
 
 // k-operand fragment from a transposed tile [rows][KT+pad]: row `row`, chunk c,
 // lane group g -> columns 16c+4g .. +3 and 16c+8+4g .. +3.
@@ -94,15 +97,19 @@ __device__ __forceinline__ typename Frag<T>::type acc_frag(const f32x16& a, int 
 
 // ------------------------------------------------------------------------
 // Forward.  grid (ceil(T/128), NH, B); heavy (late) query blocks first.
+// Per key tile: waves 0/1 bring K / V (next tile prefetched into registers),
+// K is stored row-major, V transposed.
 // ------------------------------------------------------------------------
 template <typename T, int HD>
-__global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ out,
-                                                           float* __restrict__ lse, int T_, int NH, float sl2) {
-  constexpr int VE = V16<T>::n, LDK = HD + VE, LDV = KT + VE, ND = HD / 16, NDT = HD / 32;
+__global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ out,
+                                                              float* __restrict__ lse, int T_, int NH, float sl2) {
+  typedef BlockTile<T, HD> BT;
+  constexpr int LDK = BT::LDR, LDV = BT::LDT, ND = HD / 16, NDT = HD / 32, NB = BT::NBLK;
+  static_assert(2 * NB <= NW * 64 && KT <= NW * 64, "tile loaders must fit in the block");
   typedef typename Frag<T>::type F;
   typedef typename Quad<T>::type Q;
-  __shared__ __attribute__((aligned(16))) T Ks[KT * LDK];
-  __shared__ __attribute__((aligned(16))) T Vt[HD * LDV];
+  __shared__ __attribute__((aligned(16))) T Ks[2][KT * LDK];
+  __shared__ __attribute__((aligned(16))) T Vt[2][HD * LDV];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
   const int qblk = gridDim.x - 1 - blockIdx.x;
@@ -111,6 +118,10 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const T* __restrict__
   const int q0 = qblk * NW * WQ + w * WQ;
   const bool active = q0 < T_;
   const T* base = qkv + (int64_t)b * T_ * S3;
+  const T* kbase = base + C + h * HD;
+  const T* vbase = base + 2 * C + h * HD;
+  const bool ldk = tid < NB, ldv = tid >= NB && tid < 2 * NB;
+  const int li = ldk ? tid : tid - NB;
 
   F qf[ND];
   if (active) {
@@ -123,54 +134,65 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_kernel(const T* __restrict__
   float m = -INFINITY, l = 0.f;
   const int q = q0 + lr;
 
-  const int kv_end = min(T_, (qblk + 1) * NW * WQ);
-  for (int kv0 = 0; kv0 < kv_end; kv0 += KT) {
-    __syncthreads();
-    load_rows<T, HD>(Ks, base + (int64_t)kv0 * S3 + C + h * HD, S3, tid);
-    load_rows_t<T, HD>(Vt, base + (int64_t)kv0 * S3 + 2 * C + h * HD, S3, tid);
-    __syncthreads();
-    if (!active || kv0 > q0 + WQ - 1) continue;
-    f32x16 s[2];
+  const int ntiles = min(T_, (qblk + 1) * NW * WQ) / KT;
+  BT tile;
+  if (ldk) tile.load(kbase, S3, li);
+  if (ldv) tile.load(vbase, S3, li);
+  if (ldk) tile.store_rows(Ks[0], li);
+  if (ldv) tile.store_t(Vt[0], li);
+  __syncthreads();
+  for (int it = 0; it < ntiles; it++) {
+    const int cur = it & 1, kv0 = it * KT;
+    const bool more = it + 1 < ntiles;
+    if (more && ldk) tile.load(kbase + (int64_t)(kv0 + KT) * S3, S3, li);
+    if (more && ldv) tile.load(vbase + (int64_t)(kv0 + KT) * S3, S3, li);
+    if (active && kv0 <= q0 + WQ - 1) {
+      f32x16 s[2];
 #pragma unroll
-    for (int c2 = 0; c2 < 2; c2++) {
-      s[c2] = f32x16{};
+      for (int c2 = 0; c2 < 2; c2++) {
+        s[c2] = f32x16{};
 #pragma unroll
-      for (int ds = 0; ds < ND; ds++) mma16(s[c2], ld8(Ks + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), qf[ds]);
-    }
-    // scale into the log2 domain, mask keys after the query
-    float mx = -INFINITY;
-#pragma unroll
-    for (int c2 = 0; c2 < 2; c2++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int kv = kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-        const float t = kv <= q ? s[c2][r] * sl2 : -INFINITY;
-        s[c2][r] = t;
-        mx = fmaxf(mx, t);
+        for (int ds = 0; ds < ND; ds++)
+          mma16(s[c2], ld8(Ks[cur] + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), qf[ds]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mn = fmaxf(m, mx);
-    const float alpha = exp2f(m - mn);
-    float rs = 0.f;
+      // scale into the log2 domain, mask keys after the query
+      float mx = -INFINITY;
 #pragma unroll
-    for (int c2 = 0; c2 < 2; c2++)
+      for (int c2 = 0; c2 < 2; c2++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const float p = exp2f(s[c2][r] - mn);
-        s[c2][r] = p;
-        rs += p;
+        for (int r = 0; r < 16; r++) {
+          const int kv = kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+          const float t = kv <= q ? s[c2][r] * sl2 : -INFINITY;
+          s[c2][r] = t;
+          mx = fmaxf(mx, t);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx);
+      const float alpha = exp2f(m - mn);
+      float rs = 0.f;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; c2++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const float p = exp2f(s[c2][r] - mn);
+          s[c2][r] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 32, 64);
+      l = l * alpha + rs;
+      m = mn;
+#pragma unroll
+      for (int dt = 0; dt < NDT; dt++) o[dt] *= alpha;
+#pragma unroll
+      for (int c = 0; c < KT / 16; c++) {
+        const F pf = acc_frag<T>(s[c / 2], c % 2);
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) mma16(o[dt], ld_split(Vt[cur], LDV, dt * 32 + lr, c, lg), pf);
       }
-    rs += __shfl_xor(rs, 32, 64);
-    l = l * alpha + rs;
-    m = mn;
-#pragma unroll
-    for (int dt = 0; dt < NDT; dt++) o[dt] *= alpha;
-#pragma unroll
-    for (int c = 0; c < KT / 16; c++) {
-      const F pf = acc_frag<T>(s[c / 2], c % 2);
-#pragma unroll
-      for (int dt = 0; dt < NDT; dt++) mma16(o[dt], ld_split(Vt, LDV, dt * 32 + lr, c, lg), pf);
     }
+    if (more && ldk) tile.store_rows(Ks[cur ^ 1], li);
+    if (more && ldv) tile.store_t(Vt[cur ^ 1], li);
+    __syncthreads();
   }
   if (!active) return;
   const float inv = 1.f / l;
@@ -215,17 +237,21 @@ __global__ void attn_dsum_kernel(const T* __restrict__ out, const T* __restrict_
 // ------------------------------------------------------------------------
 // dQ.  grid (ceil(T/128), NH, B).  Per query column (one per lane):
 // P^T = exp(S^T - LSE), dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ = scale dS K.
+// Per key tile: K (stored row-major and transposed) and V (row-major).
 // ------------------------------------------------------------------------
 template <typename T, int HD>
-__global__ void __launch_bounds__(NW * 64) attn_dq_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
-                                                          const float* __restrict__ lse, const float* __restrict__ dsum,
-                                                          T* __restrict__ dqkv, int T_, int NH, float sl2, float scale) {
-  constexpr int VE = V16<T>::n, LDK = HD + VE, LDV = KT + VE, ND = HD / 16, NDT = HD / 32;
+__global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
+                                                             const float* __restrict__ lse,
+                                                             const float* __restrict__ dsum, T* __restrict__ dqkv,
+                                                             int T_, int NH, float sl2, float scale) {
+  typedef BlockTile<T, HD> BT;
+  constexpr int LDK = BT::LDR, LDV = BT::LDT, ND = HD / 16, NDT = HD / 32, NB = BT::NBLK;
+  static_assert(2 * NB <= NW * 64 && KT <= NW * 64, "tile loaders must fit in the block");
   typedef typename Frag<T>::type F;
   typedef typename Quad<T>::type Q;
-  __shared__ __attribute__((aligned(16))) T Ks[KT * LDK];
-  __shared__ __attribute__((aligned(16))) T Vs[KT * LDK];
-  __shared__ __attribute__((aligned(16))) T Kt[HD * LDV];
+  __shared__ __attribute__((aligned(16))) T Ks[2][KT * LDK];
+  __shared__ __attribute__((aligned(16))) T Vs[2][KT * LDK];
+  __shared__ __attribute__((aligned(16))) T Kt[2][HD * LDV];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
   const int qblk = gridDim.x - 1 - blockIdx.x;
@@ -234,6 +260,10 @@ __global__ void __launch_bounds__(NW * 64) attn_dq_kernel(const T* __restrict__ 
   const int q0 = qblk * NW * WQ + w * WQ;
   const bool active = q0 < T_;
   const T* base = qkv + (int64_t)b * T_ * S3;
+  const T* kbase = base + C + h * HD;
+  const T* vbase = base + 2 * C + h * HD;
+  const bool ldk = tid < NB, ldv = tid >= NB && tid < 2 * NB;
+  const int li = ldk ? tid : tid - NB;
   const int q = q0 + lr;
 
   F qf[ND], df[ND];
@@ -251,37 +281,52 @@ __global__ void __launch_bounds__(NW * 64) attn_dq_kernel(const T* __restrict__ 
 #pragma unroll
   for (int dt = 0; dt < NDT; dt++) dq[dt] = f32x16{};
 
-  const int kv_end = min(T_, (qblk + 1) * NW * WQ);
-  for (int kv0 = 0; kv0 < kv_end; kv0 += KT) {
-    __syncthreads();
-    load_rows<T, HD>(Ks, base + (int64_t)kv0 * S3 + C + h * HD, S3, tid);
-    load_rows<T, HD>(Vs, base + (int64_t)kv0 * S3 + 2 * C + h * HD, S3, tid);
-    load_rows_t<T, HD>(Kt, base + (int64_t)kv0 * S3 + C + h * HD, S3, tid);
-    __syncthreads();
-    if (!active || kv0 > q0 + WQ - 1) continue;
-    f32x16 s[2], dp[2];
+  const int ntiles = min(T_, (qblk + 1) * NW * WQ) / KT;
+  BT tile;
+  if (ldk) tile.load(kbase, S3, li);
+  if (ldv) tile.load(vbase, S3, li);
+  if (ldk) {
+    tile.store_rows(Ks[0], li);
+    tile.store_t(Kt[0], li);
+  }
+  if (ldv) tile.store_rows(Vs[0], li);
+  __syncthreads();
+  for (int it = 0; it < ntiles; it++) {
+    const int cur = it & 1, kv0 = it * KT;
+    const bool more = it + 1 < ntiles;
+    if (more && ldk) tile.load(kbase + (int64_t)(kv0 + KT) * S3, S3, li);
+    if (more && ldv) tile.load(vbase + (int64_t)(kv0 + KT) * S3, S3, li);
+    if (active && kv0 <= q0 + WQ - 1) {
+      f32x16 s[2], dp[2];
 #pragma unroll
-    for (int c2 = 0; c2 < 2; c2++) {
-      s[c2] = f32x16{};
-      dp[c2] = f32x16{};
+      for (int c2 = 0; c2 < 2; c2++) {
+        s[c2] = f32x16{};
+        dp[c2] = f32x16{};
 #pragma unroll
-      for (int ds = 0; ds < ND; ds++) {
-        mma16(s[c2], ld8(Ks + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), qf[ds]);
-        mma16(dp[c2], ld8(Vs + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), df[ds]);
+        for (int ds = 0; ds < ND; ds++) {
+          mma16(s[c2], ld8(Ks[cur] + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), qf[ds]);
+          mma16(dp[c2], ld8(Vs[cur] + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), df[ds]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int kv = kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+          const float p = kv <= q ? exp2f(s[c2][r] * sl2 - lse2) : 0.f;
+          s[c2][r] = p * (dp[c2][r] - dq_d);  // dS^T
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int kv = kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-        const float p = kv <= q ? exp2f(s[c2][r] * sl2 - lse2) : 0.f;
-        s[c2][r] = p * (dp[c2][r] - dq_d);  // dS^T
+      for (int c = 0; c < KT / 16; c++) {
+        const F sf = acc_frag<T>(s[c / 2], c % 2);
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) mma16(dq[dt], ld_split(Kt[cur], LDV, dt * 32 + lr, c, lg), sf);
       }
     }
-#pragma unroll
-    for (int c = 0; c < KT / 16; c++) {
-      const F sf = acc_frag<T>(s[c / 2], c % 2);
-#pragma unroll
-      for (int dt = 0; dt < NDT; dt++) mma16(dq[dt], ld_split(Kt, LDV, dt * 32 + lr, c, lg), sf);
+    if (more && ldk) {
+      tile.store_rows(Ks[cur ^ 1], li);
+      tile.store_t(Kt[cur ^ 1], li);
     }
+    if (more && ldv) tile.store_rows(Vs[cur ^ 1], li);
+    __syncthreads();
   }
   if (!active) return;
   T* row = dqkv + ((int64_t)b * T_ + q) * S3 + h * HD;
@@ -300,19 +345,23 @@ __global__ void __launch_bounds__(NW * 64) attn_dq_kernel(const T* __restrict__ 
 // dK, dV.  grid (ceil(T/128), NH, B); each wave owns 32 keys and walks the
 // query tiles at or after them.  Per key column (one per lane):
 // P = exp(S - LSE), dV += dO^T P, dP = dO V^T, dS = P (dP - D), dK += scale Q^T dS.
+// Per query tile: Q and dO, each stored row-major and transposed; LSE and D.
 // ------------------------------------------------------------------------
 template <typename T, int HD>
 __global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
-                                                           const float* __restrict__ lse, const float* __restrict__ dsum,
-                                                           T* __restrict__ dqkv, int T_, int NH, float sl2, float scale) {
-  constexpr int VE = V16<T>::n, LDK = HD + VE, LDV = KT + VE, ND = HD / 16, NDT = HD / 32;
+                                                              const float* __restrict__ lse,
+                                                              const float* __restrict__ dsum, T* __restrict__ dqkv,
+                                                              int T_, int NH, float sl2, float scale) {
+  typedef BlockTile<T, HD> BT;
+  constexpr int LDK = BT::LDR, LDV = BT::LDT, ND = HD / 16, NDT = HD / 32, NB = BT::NBLK;
+  static_assert(2 * NB <= NW * 64 && KT <= NW * 64, "tile loaders must fit in the block");
   typedef typename Frag<T>::type F;
   typedef typename Quad<T>::type Q;
-  __shared__ __attribute__((aligned(16))) T Qs[KT * LDK];
-  __shared__ __attribute__((aligned(16))) T Ds[KT * LDK];
-  __shared__ __attribute__((aligned(16))) T Qt[HD * LDV];
-  __shared__ __attribute__((aligned(16))) T Dt[HD * LDV];
-  __shared__ float Ls[KT], Dd[KT];
+  __shared__ __attribute__((aligned(16))) T Qs[2][KT * LDK];
+  __shared__ __attribute__((aligned(16))) T Ds[2][KT * LDK];
+  __shared__ __attribute__((aligned(16))) T Qt[2][HD * LDV];
+  __shared__ __attribute__((aligned(16))) T Dt[2][HD * LDV];
+  __shared__ float Ls[2][KT], Dd[2][KT];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
   const int kblk = blockIdx.x;  // early key blocks see the most queries: they go first
@@ -321,6 +370,11 @@ __global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__
   const int k0 = kblk * NW * WQ + w * WQ;
   const bool active = k0 < T_;
   const T* base = qkv + (int64_t)b * T_ * S3;
+  const T* qbase = base + h * HD;
+  const T* obase = dout + (int64_t)b * T_ * C + h * HD;
+  const bool ldq = tid < NB, ldo = tid >= NB && tid < 2 * NB;
+  const int li = ldq ? tid : tid - NB;
+  const bool ldl = tid < KT;  // these threads also bring the tile's LSE and D values
   const int kv = k0 + lr;
 
   F kf[ND], vf[ND];
@@ -340,47 +394,81 @@ __global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__
   const float* lrow = lse + ((int64_t)b * NH + h) * T_;
   const float* drow = dsum + ((int64_t)b * NH + h) * T_;
 
-  const int q_begin = (kblk * NW * WQ / KT) * KT;
-  for (int qt0 = q_begin; qt0 < T_; qt0 += KT) {
-    __syncthreads();
-    load_rows<T, HD>(Qs, base + (int64_t)qt0 * S3 + h * HD, S3, tid);
-    load_rows<T, HD>(Ds, dout + ((int64_t)b * T_ + qt0) * C + h * HD, C, tid);
-    load_rows_t<T, HD>(Qt, base + (int64_t)qt0 * S3 + h * HD, S3, tid);
-    load_rows_t<T, HD>(Dt, dout + ((int64_t)b * T_ + qt0) * C + h * HD, C, tid);
-    if (tid < KT) {
-      Ls[tid] = lrow[qt0 + tid] * LOG2E;
-      Dd[tid] = drow[qt0 + tid];
+  const int qt_begin = (kblk * NW * WQ / KT) * KT;
+  const int ntiles = (T_ - qt_begin) / KT;
+  BT tile;
+  float sl = 0.f, sd = 0.f;
+  if (ldq) tile.load(qbase + (int64_t)qt_begin * S3, S3, li);
+  if (ldo) tile.load(obase + (int64_t)qt_begin * C, C, li);
+  if (ldl) {
+    sl = lrow[qt_begin + tid] * LOG2E;
+    sd = drow[qt_begin + tid];
+  }
+  if (ldq) {
+    tile.store_rows(Qs[0], li);
+    tile.store_t(Qt[0], li);
+  }
+  if (ldo) {
+    tile.store_rows(Ds[0], li);
+    tile.store_t(Dt[0], li);
+  }
+  if (ldl) {
+    Ls[0][tid] = sl;
+    Dd[0][tid] = sd;
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; it++) {
+    const int cur = it & 1, qt0 = qt_begin + it * KT;
+    const bool more = it + 1 < ntiles;
+    if (more && ldq) tile.load(qbase + (int64_t)(qt0 + KT) * S3, S3, li);
+    if (more && ldo) tile.load(obase + (int64_t)(qt0 + KT) * C, C, li);
+    if (more && ldl) {
+      sl = lrow[qt0 + KT + tid] * LOG2E;
+      sd = drow[qt0 + KT + tid];
+    }
+    if (active && qt0 + KT - 1 >= k0) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int c2 = 0; c2 < 2; c2++) {
+        s[c2] = f32x16{};
+        dp[c2] = f32x16{};
+#pragma unroll
+        for (int ds = 0; ds < ND; ds++) {
+          mma16(s[c2], ld8(Qs[cur] + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), kf[ds]);
+          mma16(dp[c2], ld8(Ds[cur] + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), vf[ds]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const int ql = c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+          const float p = qt0 + ql >= kv ? exp2f(s[c2][r] * sl2 - Ls[cur][ql]) : 0.f;
+          s[c2][r] = p;
+          dp[c2][r] = p * (dp[c2][r] - Dd[cur][ql]);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < KT / 16; c++) {
+        const F pf = acc_frag<T>(s[c / 2], c % 2);
+        const F sf = acc_frag<T>(dp[c / 2], c % 2);
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) {
+          mma16(dv[dt], ld_split(Dt[cur], LDV, dt * 32 + lr, c, lg), pf);
+          mma16(dk[dt], ld_split(Qt[cur], LDV, dt * 32 + lr, c, lg), sf);
+        }
+      }
+    }
+    if (more && ldq) {
+      tile.store_rows(Qs[cur ^ 1], li);
+      tile.store_t(Qt[cur ^ 1], li);
+    }
+    if (more && ldo) {
+      tile.store_rows(Ds[cur ^ 1], li);
+      tile.store_t(Dt[cur ^ 1], li);
+    }
+    if (more && ldl) {
+      Ls[cur ^ 1][tid] = sl;
+      Dd[cur ^ 1][tid] = sd;
     }
     __syncthreads();
-    if (!active || qt0 + KT - 1 < k0) continue;
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int c2 = 0; c2 < 2; c2++) {
-      s[c2] = f32x16{};
-      dp[c2] = f32x16{};
-#pragma unroll
-      for (int ds = 0; ds < ND; ds++) {
-        mma16(s[c2], ld8(Qs + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), kf[ds]);
-        mma16(dp[c2], ld8(Ds + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), vf[ds]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int ql = c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-        const float p = qt0 + ql >= kv ? exp2f(s[c2][r] * sl2 - Ls[ql]) : 0.f;
-        s[c2][r] = p;
-        dp[c2][r] = p * (dp[c2][r] - Dd[ql]);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < KT / 16; c++) {
-      const F pf = acc_frag<T>(s[c / 2], c % 2);
-      const F sf = acc_frag<T>(dp[c / 2], c % 2);
-#pragma unroll
-      for (int dt = 0; dt < NDT; dt++) {
-        mma16(dv[dt], ld_split(Dt, LDV, dt * 32 + lr, c, lg), pf);
-        mma16(dk[dt], ld_split(Qt, LDV, dt * 32 + lr, c, lg), sf);
-      }
-    }
   }
   if (!active) return;
   T* row = dqkv + ((int64_t)b * T_ + kv) * S3 + h * HD;

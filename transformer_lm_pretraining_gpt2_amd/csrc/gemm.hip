@@ -41,10 +41,9 @@ struct TileLoader<T, R, BK, LDK, NT, 0> {
     for (int c = 0; c < PER; c++) {
       const int idx = tid + c * NT;
       const int row = idx / CPR, kc = idx % CPR;
-      if (row0 + row < nrows)
-        reg[c] = *reinterpret_cast<const f32x4*>(X + (int64_t)(row0 + row) * ld + k0 + kc * VE);
-      else
-        reg[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // rows past the edge read the last row: they only feed outputs the epilogue drops
+      const int r = min(row0 + row, nrows - 1);
+      reg[c] = *reinterpret_cast<const f32x4*>(X + (int64_t)r * ld + k0 + kc * VE);
     }
   }
   __device__ __forceinline__ void store(T* s, int tid) {
@@ -75,14 +74,10 @@ struct TileLoader<T, R, BK, LDK, NT, 1> {
       const int blk = tid + c * NT;
       if (TOTAL % NT != 0 && blk >= TOTAL) continue;
       const int rb = blk / NCB, cb = blk % NCB;
-      const bool ok = row0 + cb * VE < nrows;
+      // column blocks past the edge re-read the last one (their outputs are dropped)
+      const int col = min(row0 + cb * VE, nrows - VE);
 #pragma unroll
-      for (int a = 0; a < 8; a++) {
-        if (ok)
-          reg[c][a] = *reinterpret_cast<const V*>(X + (int64_t)(k0 + rb * 8 + a) * ld + row0 + cb * VE);
-        else
-          reg[c][a] = V{};
-      }
+      for (int a = 0; a < 8; a++) reg[c][a] = *reinterpret_cast<const V*>(X + (int64_t)(k0 + rb * 8 + a) * ld + col);
     }
   }
   __device__ __forceinline__ void store(T* s, int tid) {
@@ -246,9 +241,8 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   }
 }
 
-template <typename T, int AT, int BT, int EPI>
+template <typename T, int BM, int BN, int WI, int WJ, int AT, int BT, int EPI>
 hipError_t launch(hipStream_t st, const GemmArgs& g) {
-  constexpr int BM = 128, BN = 128, WI = 2, WJ = 2;
   constexpr int BK = sizeof(T) == 2 ? 64 : 32;
   constexpr int VE = Vec16<T>::n;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
@@ -261,17 +255,44 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
   return hipGetLastError();
 }
 
+// Tile shape per operand layout and output shape (bf16), from a sweep of the
+// step's matmuls on MI355X: 256x192 where the output width is a multiple of
+// 192 up to 1536 (one wave of 256 CUs for 16384 x 768), 256x256 with eight
+// waves for wide outputs, 128x128 otherwise.
+enum TileKind { TILE_128 = 0, TILE_256x192 = 1, TILE_256_W8 = 2 };
+
+TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N) {
+  if (p != BF16 || M < 256) return TILE_128;
+  const bool narrow = N % 192 == 0 && N <= 1536;
+  if (a_t && b_t) return (int64_t)M * N >= 8000000 ? TILE_256_W8 : narrow ? TILE_256x192 : TILE_256_W8;
+  if (N >= 3072) return TILE_256_W8;
+  if (narrow) return TILE_256x192;
+  return TILE_128;
+}
+
+template <typename T, int AT, int BT, int EPI>
+hipError_t launch_tiled(hipStream_t st, const GemmArgs& g, TileKind k) {
+  if constexpr (sizeof(T) == 2) {
+    if (k == TILE_256x192) return launch<T, 256, 192, 2, 2, AT, BT, EPI>(st, g);
+    if (k == TILE_256_W8) {
+      if (AT || BT) return launch<T, 256, 256, 2, 4, AT, BT, EPI>(st, g);
+      return launch<T, 256, 256, 4, 2, AT, BT, EPI>(st, g);
+    }
+  }
+  return launch<T, 128, 128, 2, 2, AT, BT, EPI>(st, g);
+}
+
 template <typename T>
-hipError_t dispatch(hipStream_t st, int a_t, int b_t, int epi, const GemmArgs& g) {
+hipError_t dispatch(hipStream_t st, int a_t, int b_t, int epi, const GemmArgs& g, TileKind k) {
   if (!a_t && !b_t) {
-    if (epi == EPI_STORE) return launch<T, 0, 0, EPI_STORE>(st, g);
-    if (epi == EPI_GELU) return launch<T, 0, 0, EPI_GELU>(st, g);
-    if (epi == EPI_RESID) return launch<T, 0, 0, EPI_RESID>(st, g);
+    if (epi == EPI_STORE) return launch_tiled<T, 0, 0, EPI_STORE>(st, g, k);
+    if (epi == EPI_GELU) return launch_tiled<T, 0, 0, EPI_GELU>(st, g, k);
+    if (epi == EPI_RESID) return launch_tiled<T, 0, 0, EPI_RESID>(st, g, k);
   } else if (!a_t && b_t) {
-    if (epi == EPI_STORE) return launch<T, 0, 1, EPI_STORE>(st, g);
-    if (epi == EPI_GELU_BWD) return launch<T, 0, 1, EPI_GELU_BWD>(st, g);
+    if (epi == EPI_STORE) return launch_tiled<T, 0, 1, EPI_STORE>(st, g, k);
+    if (epi == EPI_GELU_BWD) return launch_tiled<T, 0, 1, EPI_GELU_BWD>(st, g, k);
   } else if (a_t && b_t) {
-    if (epi == EPI_F32) return launch<T, 1, 1, EPI_F32>(st, g);
+    if (epi == EPI_F32) return launch_tiled<T, 1, 1, EPI_F32>(st, g, k);
   }
   return hipErrorInvalidValue;
 }
@@ -279,7 +300,21 @@ hipError_t dispatch(hipStream_t st, int a_t, int b_t, int epi, const GemmArgs& g
 }  // namespace
 
 hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArgs& g) {
-  return p == BF16 ? dispatch<bf16>(st, a_t, b_t, epi, g) : dispatch<float>(st, a_t, b_t, epi, g);
+  const TileKind k = choose_tile(p, a_t, b_t, g.M, g.N);
+  return p == BF16 ? dispatch<bf16>(st, a_t, b_t, epi, g, k) : dispatch<float>(st, a_t, b_t, epi, g, k);
+}
+
+int gemm_split_hint(Prec p, int a_t, int b_t, int M, int N, int K) {
+  const TileKind k = choose_tile(p, a_t, b_t, M, N);
+  const int bm = k == TILE_128 ? 128 : 256, bn = k == TILE_256x192 ? 192 : (k == TILE_256_W8 ? 256 : 128);
+  const int bk = p == BF16 ? 64 : 32;
+  const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  // one block per CU for the large tiles, two for 128x128; the reduction must
+  // split into equal multiples of the K step
+  const int target = k == TILE_128 ? 512 : 256;
+  int s = 1;
+  while (s < 16 && tiles * s < target && K % (2 * s * bk) == 0) s *= 2;
+  return s;
 }
 
 }  // namespace gpt2k

@@ -112,15 +112,6 @@ struct Plan {
   std::vector<int> split;  // split-K factor per layer weight kind (qkv, proj, fc, fcproj)
 };
 
-constexpr int GEMM_BK_MIN = 64;
-
-int pick_splits(int tiles, int M) {
-  // enough blocks to cover the chip twice; the reduction length M must split
-  // into equal multiples of 64
-  int s = 1;
-  while (s < 16 && tiles * s < 512 && (M % (2 * s * GEMM_BK_MIN)) == 0) s *= 2;
-  return s;
-}
 
 Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
   Plan P;
@@ -160,8 +151,10 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
   P.du = take(a * M * 4 * C);
   P.dsum = take(4 * M * NH);
   P.piece = take(4 * M * C);
-  const int tq = (int)((3 * C / 128) * (C / 128)), tp = (int)((C / 128) * (C / 128)), tf = (int)((4 * C / 128) * (C / 128));
-  P.split = {pick_splits(tq, (int)M), pick_splits(tp, (int)M), pick_splits(tf, (int)M), pick_splits(tf, (int)M)};
+  const Prec pr = prec == GPT2_BF16 ? BF16 : F32;
+  const int Mi = (int)M, Ci = (int)C;
+  P.split = {gemm_split_hint(pr, 1, 1, 3 * Ci, Ci, Mi), gemm_split_hint(pr, 1, 1, Ci, Ci, Mi),
+             gemm_split_hint(pr, 1, 1, 4 * Ci, Ci, Mi), gemm_split_hint(pr, 1, 1, Ci, 4 * Ci, Mi)};
   int64_t wmax = 0;
   const int64_t wsz[4] = {3 * C * C, C * C, 4 * C * C, 4 * C * C};
   for (int k = 0; k < 4; k++) wmax = std::max(wmax, (int64_t)P.split[k] * wsz[k]);

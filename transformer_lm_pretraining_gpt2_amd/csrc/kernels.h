@@ -37,6 +37,8 @@ struct GemmArgs {
 };
 
 hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArgs& g);
+// split-K factor that fills the chip for an M x N x K weight-gradient product
+int gemm_split_hint(Prec p, int a_t, int b_t, int M, int N, int K);
 
 // ---- attention (causal, packed qkv [B*T, 3C]: q heads | k heads | v heads) ----
 hipError_t attn_fwd(hipStream_t st, Prec p, const void* qkv, void* out, float* lse, int B, int T, int NH, int hd);

@@ -158,14 +158,30 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const T* __restrict__ dy, c
     part[(int64_t)blockIdx.x * 2 * C + j] = ((sh[j] + sh[2 * C + j]) + sh[4 * C + j]) + sh[6 * C + j];
 }
 
-// out[j] = [out[j] +] sum_p part[p*ld + j], p in index order
-__global__ void reduce_parts_kernel(const float* __restrict__ part, int nparts, int64_t ld, float* __restrict__ out,
-                                    int n, int accumulate) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= n) return;
-  float s = 0.f;
-  for (int p = 0; p < nparts; p++) s += part[(int64_t)p * ld + j];
-  out[j] = accumulate ? out[j] + s : s;
+// out[j] = [out[j] +] sum_p part[p*ld + j].  A block of 16 waves covers 256
+// consecutive j (four per lane); wave w sums its contiguous range of p in
+// order, then the 16 wave sums are added in wave order.
+constexpr int RED_W = 16;
+
+__global__ void __launch_bounds__(RED_W * 64) reduce_parts_kernel(const float* __restrict__ part, int nparts,
+                                                                  int64_t ld, float* __restrict__ out, int n,
+                                                                  int accumulate) {
+  __shared__ f32x4 sh[RED_W][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t j = ((int64_t)blockIdx.x * 64 + lane) * 4;
+  const int p0 = (int)((int64_t)nparts * w / RED_W), p1 = (int)((int64_t)nparts * (w + 1) / RED_W);
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  if (j < n)
+    for (int p = p0; p < p1; p++) s += *reinterpret_cast<const f32x4*>(part + (int64_t)p * ld + j);
+  sh[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && j < n) {
+    f32x4 t = sh[0][lane];
+#pragma unroll
+    for (int k = 1; k < RED_W; k++) t += sh[k][lane];
+    if (accumulate) t += *reinterpret_cast<const f32x4*>(out + j);
+    *reinterpret_cast<f32x4*>(out + j) = t;
+  }
 }
 
 // part[chunk][j] = sum over rows of the chunk of X[row][j] (rows in order)
@@ -591,7 +607,9 @@ hipError_t layernorm_bwd(hipStream_t st, Prec p, const void* dy, const float* x,
 }
 
 hipError_t reduce_parts(hipStream_t st, const float* part, int nparts, int64_t ld, float* out, int n, int accumulate) {
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3((n + 255) / 256), dim3(256), 0, st, part, nparts, ld, out, n, accumulate);
+  if (n % 4 != 0 || ld % 4 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3((n / 4 + 63) / 64), dim3(RED_W * 64), 0, st, part, nparts, ld, out, n,
+                     accumulate);
   return hipGetLastError();
 }
 
