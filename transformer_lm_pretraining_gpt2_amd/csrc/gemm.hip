@@ -22,77 +22,76 @@ template <typename T> struct Vec16;  // 16 bytes of T
 template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int n = 8; };
 template <> struct Vec16<float> { typedef f32x4 type; static constexpr int n = 4; };
 
-// Global -> LDS loader of one R x BK operand tile, LDS layout [R][LDK] with
-// the reduction index contiguous.
-template <typename T, int R, int BK, int LDK, int NT, int TRANS>
-struct TileLoader;
+// One operand tile (R output rows x BK reduction) on its way global ->
+// registers -> LDS, and the MFMA fragments read back from LDS.
+//  TRANS = 0: X(row, r) = X[row*ld + r]; LDS [R][BK + VE]  (reduction contiguous,
+//             16-byte row pad keeps the fragment reads free of bank conflicts)
+//  TRANS = 1: X(row, r) = X[r*ld + row]; LDS [BK][R + PADR] (kept in the global
+//             layout; bf16 fragments come from the transposing LDS read
+//             ds_read_b64_tr_b16, fp32 fragments from scalar reads)
+// Both layouts are filled with plain 16-byte copies.
+constexpr int PADR = 32;  // elements; a 64-byte pad puts the 4 rows one transposing read touches in distinct banks
 
-// Reduction index contiguous in memory: X(row, r) = X[row*ld + r].
-template <typename T, int R, int BK, int LDK, int NT>
-struct TileLoader<T, R, BK, LDK, NT, 0> {
+template <typename T, int R, int BK, int NT, int TRANS>
+struct Operand {
   static constexpr int VE = Vec16<T>::n;
-  static constexpr int CPR = BK / VE;
-  static constexpr int TOTAL = R * CPR;
-  static constexpr int PER = TOTAL / NT;
-  static_assert(TOTAL % NT == 0, "tile does not split evenly over threads");
-  f32x4 reg[PER];
-  __device__ __forceinline__ void load(const T* X, int64_t ld, int row0, int nrows, int k0, int tid) {
-#pragma unroll
-    for (int c = 0; c < PER; c++) {
-      const int idx = tid + c * NT;
-      const int row = idx / CPR, kc = idx % CPR;
-      // rows past the edge read the last row: they only feed outputs the epilogue drops
-      const int r = min(row0 + row, nrows - 1);
-      reg[c] = *reinterpret_cast<const f32x4*>(X + (int64_t)r * ld + k0 + kc * VE);
-    }
-  }
-  __device__ __forceinline__ void store(T* s, int tid) {
-#pragma unroll
-    for (int c = 0; c < PER; c++) {
-      const int idx = tid + c * NT;
-      const int row = idx / CPR, kc = idx % CPR;
-      *reinterpret_cast<f32x4*>(s + row * LDK + kc * VE) = reg[c];
-    }
-  }
-};
-
-// Reduction index strided: X(row, r) = X[r*ld + row].  Each thread moves an
-// 8 (r) x VE (rows) block: eight 16-byte loads along rows, an in-register
-// transpose, then VE stores of 8 consecutive r values.
-template <typename T, int R, int BK, int LDK, int NT>
-struct TileLoader<T, R, BK, LDK, NT, 1> {
-  typedef typename Vec16<T>::type V;
+  static constexpr int LD = TRANS ? R + PADR : BK + VE;         // LDS row length (elements)
+  static constexpr int ELEMS = TRANS ? BK * LD : R * LD;        // LDS tile size (elements)
+  static constexpr int CPR = TRANS ? R / VE : BK / VE;          // 16-byte chunks per global row
+  static constexpr int PER = R * BK / VE / NT;                  // chunks per thread
+  static_assert((R * BK / VE) % NT == 0, "tile does not split evenly over threads");
   typedef typename Frag<T>::type F;
-  static constexpr int VE = Vec16<T>::n;
-  static constexpr int NCB = R / VE;
-  static constexpr int TOTAL = (BK / 8) * NCB;
-  static constexpr int PER = (TOTAL + NT - 1) / NT;
-  V reg[PER][8];
+  f32x4 reg[PER];
+
   __device__ __forceinline__ void load(const T* X, int64_t ld, int row0, int nrows, int k0, int tid) {
 #pragma unroll
     for (int c = 0; c < PER; c++) {
-      const int blk = tid + c * NT;
-      if (TOTAL % NT != 0 && blk >= TOTAL) continue;
-      const int rb = blk / NCB, cb = blk % NCB;
-      // column blocks past the edge re-read the last one (their outputs are dropped)
-      const int col = min(row0 + cb * VE, nrows - VE);
-#pragma unroll
-      for (int a = 0; a < 8; a++) reg[c][a] = *reinterpret_cast<const V*>(X + (int64_t)(k0 + rb * 8 + a) * ld + col);
+      const int idx = tid + c * NT;
+      const int gr = idx / CPR, gc = idx % CPR;
+      if constexpr (TRANS == 0) {
+        // rows past the edge re-read the last row: they only feed outputs the epilogue drops
+        const int r = min(row0 + gr, nrows - 1);
+        reg[c] = *reinterpret_cast<const f32x4*>(X + (int64_t)r * ld + k0 + gc * VE);
+      } else {
+        const int col = min(row0 + gc * VE, nrows - VE);
+        reg[c] = *reinterpret_cast<const f32x4*>(X + (int64_t)(k0 + gr) * ld + col);
+      }
     }
   }
-  __device__ __forceinline__ void store(T* s, int tid) {
+  __device__ __forceinline__ void store(T* s, int tid) const {
 #pragma unroll
     for (int c = 0; c < PER; c++) {
-      const int blk = tid + c * NT;
-      if (TOTAL % NT != 0 && blk >= TOTAL) continue;
-      const int rb = blk / NCB, cb = blk % NCB;
+      const int idx = tid + c * NT;
+      const int gr = idx / CPR, gc = idx % CPR;
+      *reinterpret_cast<f32x4*>(s + gr * LD + gc * VE) = reg[c];
+    }
+  }
+  // Fragment of substep ks for rows rb .. rb+31: lane l gets row rb + l%32 and
+  // reduction values 16*ks + 8*(l/32) + 0..7.
+  static __device__ __forceinline__ F frag(const T* s, int rb, int ks, int lane) {
+    if constexpr (TRANS == 0) {
+      return ld8(s + (rb + (lane & 31)) * LD + ks * 16 + 8 * (lane >> 5));
+    } else if constexpr (sizeof(T) == 2) {
+      // within each 16-lane group, lane j points at row r0 + j/4, columns
+      // c0 + 4*(j%4) .. +3; the transposing read hands lane i the four rows at
+      // column c0 + i
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const int j = lane & 15;
+      const int kr = ks * 16 + 8 * (lane >> 5) + (j >> 2);
+      const int col = rb + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+      const T* p = s + kr * LD + col;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * LD));
+      // whole-vector bit casts (element-wise casts of these vectors miscompile)
+      const bf16x4 a = __builtin_bit_cast(bf16x4, lo), b = __builtin_bit_cast(bf16x4, hi);
+      return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    } else {
+      F f;
+      const T* p = s + (ks * 16 + 8 * (lane >> 5)) * LD + rb + (lane & 31);
 #pragma unroll
-      for (int b = 0; b < VE; b++) {
-        F w;
-#pragma unroll
-        for (int a = 0; a < 8; a++) w[a] = reg[c][a][b];
-        st8(s + (cb * VE + b) * LDK + rb * 8, w);
-      }
+      for (int e = 0; e < 8; e++) f[e] = p[e * LD];
+      return f;
     }
   }
 };
@@ -100,14 +99,14 @@ struct TileLoader<T, R, BK, LDK, NT, 1> {
 template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI>
 __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   constexpr int NT = WI * WJ * 64;
-  constexpr int VE = Vec16<T>::n;
-  constexpr int LDK = BK + VE;  // 16 bytes of row padding against LDS bank conflicts
   constexpr int WTI = BM / WI, WTJ = BN / WJ;
   constexpr int TI = WTI / 32, TJ = WTJ / 32;
+  typedef Operand<T, BM, BK, NT, AT> OA;
+  typedef Operand<T, BN, BK, NT, BT> OB;
   typedef typename Frag<T>::type F;
   typedef typename Quad<T>::type Q;
-  __shared__ __attribute__((aligned(16))) T sA[2][BM * LDK];
-  __shared__ __attribute__((aligned(16))) T sB[2][BN * LDK];
+  __shared__ __attribute__((aligned(16))) T sA[2][OA::ELEMS];
+  __shared__ __attribute__((aligned(16))) T sB[2][OB::ELEMS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = wave / WJ, wj = wave % WJ;
@@ -128,48 +127,62 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   const T* A = static_cast<const T*>(g.A);
   const T* Bm = static_cast<const T*>(g.B);
 
-  TileLoader<T, BM, BK, LDK, NT, AT> la;
-  TileLoader<T, BN, BK, LDK, NT, BT> lb;
   f32x16 acc[TI][TJ];
 #pragma unroll
   for (int ti = 0; ti < TI; ti++)
 #pragma unroll
     for (int tj = 0; tj < TJ; tj++) acc[ti][tj] = f32x16{};
 
-  la.load(A, g.lda, i0, g.M, kbeg, tid);
-  lb.load(Bm, g.ldb, j0, g.N, kbeg, tid);
-  la.store(sA[0], tid);
-  lb.store(sB[0], tid);
-  __syncthreads();
+#define GEMM_COMPUTE(AS, BS)                                                                      \
+  _Pragma("unroll") for (int ks = 0; ks < BK / 16; ks++) {                                        \
+    F fa[TI], fb[TJ];                                                                             \
+    _Pragma("unroll") for (int ti = 0; ti < TI; ti++) fa[ti] = OA::frag(AS, wi * WTI + ti * 32, ks, lane); \
+    _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) fb[tj] = OB::frag(BS, wj * WTJ + tj * 32, ks, lane); \
+    _Pragma("unroll") for (int ti = 0; ti < TI; ti++)                                             \
+      _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) mma16(acc[ti][tj], fb[tj], fa[ti]);       \
+  }
 
-  const int lr = lane & 31, lg = lane >> 5;
-  for (int kt = 0; kt < nk; kt++) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      la.load(A, g.lda, i0, g.M, kbeg + (kt + 1) * BK, tid);
-      lb.load(Bm, g.ldb, j0, g.N, kbeg + (kt + 1) * BK, tid);
+  // Two register stages: the tile two steps ahead is loaded while the current
+  // one is consumed from LDS and the next one is stored to the other buffer.
+  OA a0, a1;
+  OB b0, b1;
+  a0.load(A, g.lda, i0, g.M, kbeg, tid);
+  b0.load(Bm, g.ldb, j0, g.N, kbeg, tid);
+  if (nk > 1) {
+    a1.load(A, g.lda, i0, g.M, kbeg + BK, tid);
+    b1.load(Bm, g.ldb, j0, g.N, kbeg + BK, tid);
+  }
+  a0.store(sA[0], tid);
+  b0.store(sB[0], tid);
+  __syncthreads();
+  for (int kt = 0; kt + 2 <= nk; kt += 2) {
+    // buffer 0 holds tile kt, registers 1 hold tile kt+1
+    if (kt + 2 < nk) {
+      a0.load(A, g.lda, i0, g.M, kbeg + (kt + 2) * BK, tid);
+      b0.load(Bm, g.ldb, j0, g.N, kbeg + (kt + 2) * BK, tid);
     }
-    const T* as = sA[cur];
-    const T* bs = sB[cur];
-#pragma unroll
-    for (int s = 0; s < BK / 16; s++) {
-      F fa[TI], fb[TJ];
-#pragma unroll
-      for (int ti = 0; ti < TI; ti++) fa[ti] = ld8(as + (wi * WTI + ti * 32 + lr) * LDK + s * 16 + 8 * lg);
-#pragma unroll
-      for (int tj = 0; tj < TJ; tj++) fb[tj] = ld8(bs + (wj * WTJ + tj * 32 + lr) * LDK + s * 16 + 8 * lg);
-#pragma unroll
-      for (int ti = 0; ti < TI; ti++)
-#pragma unroll
-        for (int tj = 0; tj < TJ; tj++) mma16(acc[ti][tj], fb[tj], fa[ti]);
+    GEMM_COMPUTE(sA[0], sB[0])
+    a1.store(sA[1], tid);
+    b1.store(sB[1], tid);
+    __syncthreads();
+    // buffer 1 holds tile kt+1, registers 0 hold tile kt+2
+    if (kt + 3 < nk) {
+      a1.load(A, g.lda, i0, g.M, kbeg + (kt + 3) * BK, tid);
+      b1.load(Bm, g.ldb, j0, g.N, kbeg + (kt + 3) * BK, tid);
     }
-    if (kt + 1 < nk) {
-      la.store(sA[cur ^ 1], tid);
-      lb.store(sB[cur ^ 1], tid);
+    GEMM_COMPUTE(sA[1], sB[1])
+    if (kt + 2 < nk) {
+      a0.store(sA[0], tid);
+      b0.store(sB[0], tid);
     }
     __syncthreads();
   }
+  if (nk & 1) {  // the last tile sits in buffer 0
+    GEMM_COMPUTE(sA[0], sB[0])
+  }
 
+#undef GEMM_COMPUTE
+  const int lr = lane & 31, lg = lane >> 5;
   // Epilogue: accumulator r of lane l holds out[i][j] with
   // i = tile row base + l%32, j = tile col base + 8*(r/4) + 4*(l/32) + r%4.
 #pragma unroll
@@ -256,17 +269,16 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
 }
 
 // Tile shape per operand layout and output shape (bf16), from a sweep of the
-// step's matmuls on MI355X: 256x192 where the output width is a multiple of
-// 192 up to 1536 (one wave of 256 CUs for 16384 x 768), 256x256 with eight
-// waves for wide outputs, 128x128 otherwise.
+// step's matmuls on MI355X: 256x192 (4 waves) wherever the output width is a
+// multiple of 192, 256x256 with 8 waves for the large weight gradient (tied
+// output layer), 128x128 otherwise.  The weight-gradient split-K factor is
+// chosen so every configuration fills the 256 CUs.
 enum TileKind { TILE_128 = 0, TILE_256x192 = 1, TILE_256_W8 = 2 };
 
 TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N) {
   if (p != BF16 || M < 256) return TILE_128;
-  const bool narrow = N % 192 == 0 && N <= 1536;
-  if (a_t && b_t) return (int64_t)M * N >= 8000000 ? TILE_256_W8 : narrow ? TILE_256x192 : TILE_256_W8;
-  if (N >= 3072) return TILE_256_W8;
-  if (narrow) return TILE_256x192;
+  if (a_t && b_t && (int64_t)M * N >= 8000000) return TILE_256_W8;
+  if (N % 192 == 0) return TILE_256x192;
   return TILE_128;
 }
 
@@ -274,10 +286,8 @@ template <typename T, int AT, int BT, int EPI>
 hipError_t launch_tiled(hipStream_t st, const GemmArgs& g, TileKind k) {
   if constexpr (sizeof(T) == 2) {
     if (k == TILE_256x192) return launch<T, 256, 192, 2, 2, AT, BT, EPI>(st, g);
-    if (k == TILE_256_W8) {
-      if (AT || BT) return launch<T, 256, 256, 2, 4, AT, BT, EPI>(st, g);
-      return launch<T, 256, 256, 4, 2, AT, BT, EPI>(st, g);
-    }
+    if constexpr (AT && BT)
+      if (k == TILE_256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI>(st, g);
   }
   return launch<T, 128, 128, 2, 2, AT, BT, EPI>(st, g);
 }
