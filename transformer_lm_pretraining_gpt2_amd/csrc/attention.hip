@@ -36,52 +36,53 @@ template <typename T> struct V16;
 template <> struct V16<bf16> { typedef bf16x8 type; static constexpr int n = 8; };
 template <> struct V16<float> { typedef f32x4 type; static constexpr int n = 4; };
 
-// One KT x HD row tile (rows `ld` apart in global memory) held in registers
-// as 8 (rows) x VE (columns) blocks, one block per thread of [t0, t0 + NBLK).
-// It is read from global memory once and can be written to LDS row-major
-// ([KT][HD+pad]) and/or transposed ([HD][KT+pad]); loading the next tile
-// while the current one is consumed hides the memory latency.
+// One KT x HD row tile (rows `ld` apart in global memory) held in registers,
+// spread over all threads of the block as 16-byte chunks; stored to LDS
+// row-major [KT][HD + VE].  Loading the next tile while the current one is
+// consumed hides the memory latency.
 template <typename T, int HD>
-struct BlockTile {
-  typedef typename V16<T>::type V;
-  typedef typename Frag<T>::type F;
-  static constexpr int VE = V16<T>::n, NCB = HD / VE, NBLK = (KT / 8) * NCB;
-  static constexpr int LDR = HD + VE, LDT = KT + VE;
-  V v[8];
-  __device__ __forceinline__ void load(const T* g, int64_t ld, int i) {
-    const int rb = i / NCB, cb = i % NCB;
+struct RowTile {
+  static constexpr int VE = V16<T>::n, LD = HD + VE, CPR = HD / VE, PER = KT * CPR / (NW * 64);
+  static_assert(KT * CPR % (NW * 64) == 0, "tile must split evenly over the block");
+  f32x4 v[PER];
+  __device__ __forceinline__ void load(const T* g, int64_t ld, int tid) {
 #pragma unroll
-    for (int a = 0; a < 8; a++) v[a] = *reinterpret_cast<const V*>(g + (int64_t)(rb * 8 + a) * ld + cb * VE);
+    for (int c = 0; c < PER; c++) {
+      const int idx = tid + c * NW * 64, r = idx / CPR, k = idx % CPR;
+      v[c] = *reinterpret_cast<const f32x4*>(g + (int64_t)r * ld + k * VE);
+    }
   }
-  __device__ __forceinline__ void store_rows(T* s, int i) const {
-    const int rb = i / NCB, cb = i % NCB;
+  __device__ __forceinline__ void store(T* s, int tid) const {
 #pragma unroll
-    for (int a = 0; a < 8; a++) *reinterpret_cast<V*>(s + (rb * 8 + a) * LDR + cb * VE) = v[a];
-  }
-  __device__ __forceinline__ void store_t(T* s, int i) const {
-    const int rb = i / NCB, cb = i % NCB;
-#pragma unroll
-    for (int b = 0; b < VE; b++) {
-      F w;
-#pragma unroll
-      for (int a = 0; a < 8; a++) w[a] = v[a][b];
-      st8(s + (cb * VE + b) * LDT + rb * 8, w);
+    for (int c = 0; c < PER; c++) {
+      const int idx = tid + c * NW * 64, r = idx / CPR, k = idx % CPR;
+      *reinterpret_cast<f32x4*>(s + r * LD + k * VE) = v[c];
     }
   }
 };
 
-// k-operand fragment from a transposed tile [rows][KT+pad]: row `row`, chunk c,
-// lane group g -> columns 16c+4g .. +3 and 16c+8+4g .. +3.
-template <typename T>
-__device__ __forceinline__ typename Frag<T>::type ld_split(const T* s, int ldr, int row, int c, int g) {
-  typedef typename Quad<T>::type Q;
-  const Q lo = *reinterpret_cast<const Q*>(s + row * ldr + 16 * c + 4 * g);
-  const Q hi = *reinterpret_cast<const Q*>(s + row * ldr + 16 * c + 8 + 4 * g);
+// k-operand fragment of X^T read from a row-major tile X [KT][LD]: lane l
+// gets column d = dbase + l%32 and the 8 rows key(c, g, s) = 16c + 8(s/4) +
+// 4g + s%4 (g = l/32).  bf16 uses the transposing LDS read: within each
+// 16-lane group, lane j points at row r0 + j/4, columns c0 + 4*(j%4) .. +3
+// and receives rows r0 .. r0+3 of column c0 + j.
+template <typename T, int LD>
+__device__ __forceinline__ typename Frag<T>::type ld_tsplit(const T* s, int dbase, int c, int lane) {
   typename Frag<T>::type f;
+  if constexpr (sizeof(T) == 2) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int j = lane & 15, G = lane >> 4;
+    const int r0 = 16 * c + 4 * (G >> 1) + (j >> 2);
+    const int col = dbase + 16 * (G & 1) + 4 * (j & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s + r0 * LD + col));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s + (r0 + 8) * LD + col));
+    const bf16x4 a = __builtin_bit_cast(bf16x4, lo), b = __builtin_bit_cast(bf16x4, hi);
+    f = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    const int d = dbase + (lane & 31), g = lane >> 5;
 #pragma unroll
-  for (int e = 0; e < 4; e++) {
-    f[e] = lo[e];
-    f[4 + e] = hi[e];
+    for (int e = 0; e < 8; e++) f[e] = s[(16 * c + 8 * (e / 4) + 4 * g + (e % 4)) * LD + d];
   }
   return f;
 }
@@ -95,21 +96,21 @@ __device__ __forceinline__ typename Frag<T>::type acc_frag(const f32x16& a, int 
   return f;
 }
 
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ------------------------------------------------------------------------
 // Forward.  grid (ceil(T/128), NH, B); heavy (late) query blocks first.
-// Per key tile: waves 0/1 bring K / V (next tile prefetched into registers),
-// K is stored row-major, V transposed.
+// Per key tile: K and V rows (next tile prefetched into registers).
 // ------------------------------------------------------------------------
 template <typename T, int HD>
 __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ out,
                                                               float* __restrict__ lse, int T_, int NH, float sl2) {
-  typedef BlockTile<T, HD> BT;
-  constexpr int LDK = BT::LDR, LDV = BT::LDT, ND = HD / 16, NDT = HD / 32, NB = BT::NBLK;
-  static_assert(2 * NB <= NW * 64 && KT <= NW * 64, "tile loaders must fit in the block");
+  typedef RowTile<T, HD> RT;
+  constexpr int LD = RT::LD, ND = HD / 16, NDT = HD / 32;
   typedef typename Frag<T>::type F;
   typedef typename Quad<T>::type Q;
-  __shared__ __attribute__((aligned(16))) T Ks[2][KT * LDK];
-  __shared__ __attribute__((aligned(16))) T Vt[2][HD * LDV];
+  __shared__ __attribute__((aligned(16))) T Ks[2][KT * LD];
+  __shared__ __attribute__((aligned(16))) T Vs[2][KT * LD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
   const int qblk = gridDim.x - 1 - blockIdx.x;
@@ -120,8 +121,6 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const T* __restric
   const T* base = qkv + (int64_t)b * T_ * S3;
   const T* kbase = base + C + h * HD;
   const T* vbase = base + 2 * C + h * HD;
-  const bool ldk = tid < NB, ldv = tid >= NB && tid < 2 * NB;
-  const int li = ldk ? tid : tid - NB;
 
   F qf[ND];
   if (active) {
@@ -131,50 +130,52 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const T* __restric
   f32x16 o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; dt++) o[dt] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;  // running max and sum, log2 domain
   const int q = q0 + lr;
 
   const int ntiles = min(T_, (qblk + 1) * NW * WQ) / KT;
-  BT tile;
-  if (ldk) tile.load(kbase, S3, li);
-  if (ldv) tile.load(vbase, S3, li);
-  if (ldk) tile.store_rows(Ks[0], li);
-  if (ldv) tile.store_t(Vt[0], li);
+  RT kt, vt;
+  kt.load(kbase, S3, tid);
+  vt.load(vbase, S3, tid);
+  kt.store(Ks[0], tid);
+  vt.store(Vs[0], tid);
   __syncthreads();
   for (int it = 0; it < ntiles; it++) {
     const int cur = it & 1, kv0 = it * KT;
     const bool more = it + 1 < ntiles;
-    if (more && ldk) tile.load(kbase + (int64_t)(kv0 + KT) * S3, S3, li);
-    if (more && ldv) tile.load(vbase + (int64_t)(kv0 + KT) * S3, S3, li);
+    if (more) {
+      kt.load(kbase + (int64_t)(kv0 + KT) * S3, S3, tid);
+      vt.load(vbase + (int64_t)(kv0 + KT) * S3, S3, tid);
+    }
     if (active && kv0 <= q0 + WQ - 1) {
       f32x16 s[2];
 #pragma unroll
       for (int c2 = 0; c2 < 2; c2++) {
         s[c2] = f32x16{};
 #pragma unroll
-        for (int ds = 0; ds < ND; ds++)
-          mma16(s[c2], ld8(Ks[cur] + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), qf[ds]);
+        for (int ds = 0; ds < ND; ds++) mma16(s[c2], ld8(Ks[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), qf[ds]);
       }
-      // scale into the log2 domain, mask keys after the query
+      if (kv0 + KT - 1 > q0) {  // diagonal tile: hide keys after the query
+#pragma unroll
+        for (int c2 = 0; c2 < 2; c2++)
+#pragma unroll
+          for (int r = 0; r < 16; r++)
+            if (kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4) > q) s[c2][r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int c2 = 0; c2 < 2; c2++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int kv = kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          const float t = kv <= q ? s[c2][r] * sl2 : -INFINITY;
-          s[c2][r] = t;
-          mx = fmaxf(mx, t);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[c2][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
       const float mn = fmaxf(m, mx);
-      const float alpha = exp2f(m - mn);
+      const float alpha = fast_exp2(m - mn);
       float rs = 0.f;
 #pragma unroll
       for (int c2 = 0; c2 < 2; c2++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-          const float p = exp2f(s[c2][r] - mn);
+          const float p = fast_exp2(fmaf(s[c2][r], sl2, -mn));
           s[c2][r] = p;
           rs += p;
         }
@@ -187,11 +188,13 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const T* __restric
       for (int c = 0; c < KT / 16; c++) {
         const F pf = acc_frag<T>(s[c / 2], c % 2);
 #pragma unroll
-        for (int dt = 0; dt < NDT; dt++) mma16(o[dt], ld_split(Vt[cur], LDV, dt * 32 + lr, c, lg), pf);
+        for (int dt = 0; dt < NDT; dt++) mma16(o[dt], ld_tsplit<T, LD>(Vs[cur], dt * 32, c, lane), pf);
       }
     }
-    if (more && ldk) tile.store_rows(Ks[cur ^ 1], li);
-    if (more && ldv) tile.store_t(Vt[cur ^ 1], li);
+    if (more) {
+      kt.store(Ks[cur ^ 1], tid);
+      vt.store(Vs[cur ^ 1], tid);
+    }
     __syncthreads();
   }
   if (!active) return;
@@ -237,21 +240,19 @@ __global__ void attn_dsum_kernel(const T* __restrict__ out, const T* __restrict_
 // ------------------------------------------------------------------------
 // dQ.  grid (ceil(T/128), NH, B).  Per query column (one per lane):
 // P^T = exp(S^T - LSE), dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ = scale dS K.
-// Per key tile: K (stored row-major and transposed) and V (row-major).
+// Per key tile: K and V rows; K^T fragments come from transposing reads.
 // ------------------------------------------------------------------------
 template <typename T, int HD>
 __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
                                                              const float* __restrict__ lse,
                                                              const float* __restrict__ dsum, T* __restrict__ dqkv,
                                                              int T_, int NH, float sl2, float scale) {
-  typedef BlockTile<T, HD> BT;
-  constexpr int LDK = BT::LDR, LDV = BT::LDT, ND = HD / 16, NDT = HD / 32, NB = BT::NBLK;
-  static_assert(2 * NB <= NW * 64 && KT <= NW * 64, "tile loaders must fit in the block");
+  typedef RowTile<T, HD> RT;
+  constexpr int LD = RT::LD, ND = HD / 16, NDT = HD / 32;
   typedef typename Frag<T>::type F;
   typedef typename Quad<T>::type Q;
-  __shared__ __attribute__((aligned(16))) T Ks[2][KT * LDK];
-  __shared__ __attribute__((aligned(16))) T Vs[2][KT * LDK];
-  __shared__ __attribute__((aligned(16))) T Kt[2][HD * LDV];
+  __shared__ __attribute__((aligned(16))) T Ks[2][KT * LD];
+  __shared__ __attribute__((aligned(16))) T Vs[2][KT * LD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
   const int qblk = gridDim.x - 1 - blockIdx.x;
@@ -262,8 +263,6 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
   const T* base = qkv + (int64_t)b * T_ * S3;
   const T* kbase = base + C + h * HD;
   const T* vbase = base + 2 * C + h * HD;
-  const bool ldk = tid < NB, ldv = tid >= NB && tid < 2 * NB;
-  const int li = ldk ? tid : tid - NB;
   const int q = q0 + lr;
 
   F qf[ND], df[ND];
@@ -282,21 +281,21 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
   for (int dt = 0; dt < NDT; dt++) dq[dt] = f32x16{};
 
   const int ntiles = min(T_, (qblk + 1) * NW * WQ) / KT;
-  BT tile;
-  if (ldk) tile.load(kbase, S3, li);
-  if (ldv) tile.load(vbase, S3, li);
-  if (ldk) {
-    tile.store_rows(Ks[0], li);
-    tile.store_t(Kt[0], li);
-  }
-  if (ldv) tile.store_rows(Vs[0], li);
+  RT kt, vt;
+  kt.load(kbase, S3, tid);
+  vt.load(vbase, S3, tid);
+  kt.store(Ks[0], tid);
+  vt.store(Vs[0], tid);
   __syncthreads();
   for (int it = 0; it < ntiles; it++) {
     const int cur = it & 1, kv0 = it * KT;
     const bool more = it + 1 < ntiles;
-    if (more && ldk) tile.load(kbase + (int64_t)(kv0 + KT) * S3, S3, li);
-    if (more && ldv) tile.load(vbase + (int64_t)(kv0 + KT) * S3, S3, li);
+    if (more) {
+      kt.load(kbase + (int64_t)(kv0 + KT) * S3, S3, tid);
+      vt.load(vbase + (int64_t)(kv0 + KT) * S3, S3, tid);
+    }
     if (active && kv0 <= q0 + WQ - 1) {
+      const bool diag = kv0 + KT - 1 > q0;
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int c2 = 0; c2 < 2; c2++) {
@@ -304,13 +303,13 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
         dp[c2] = f32x16{};
 #pragma unroll
         for (int ds = 0; ds < ND; ds++) {
-          mma16(s[c2], ld8(Ks[cur] + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), qf[ds]);
-          mma16(dp[c2], ld8(Vs[cur] + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), df[ds]);
+          mma16(s[c2], ld8(Ks[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), qf[ds]);
+          mma16(dp[c2], ld8(Vs[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), df[ds]);
         }
 #pragma unroll
         for (int r = 0; r < 16; r++) {
-          const int kv = kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          const float p = kv <= q ? exp2f(s[c2][r] * sl2 - lse2) : 0.f;
+          float p = fast_exp2(fmaf(s[c2][r], sl2, -lse2));
+          if (diag && kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4) > q) p = 0.f;
           s[c2][r] = p * (dp[c2][r] - dq_d);  // dS^T
         }
       }
@@ -318,14 +317,13 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
       for (int c = 0; c < KT / 16; c++) {
         const F sf = acc_frag<T>(s[c / 2], c % 2);
 #pragma unroll
-        for (int dt = 0; dt < NDT; dt++) mma16(dq[dt], ld_split(Kt[cur], LDV, dt * 32 + lr, c, lg), sf);
+        for (int dt = 0; dt < NDT; dt++) mma16(dq[dt], ld_tsplit<T, LD>(Ks[cur], dt * 32, c, lane), sf);
       }
     }
-    if (more && ldk) {
-      tile.store_rows(Ks[cur ^ 1], li);
-      tile.store_t(Kt[cur ^ 1], li);
+    if (more) {
+      kt.store(Ks[cur ^ 1], tid);
+      vt.store(Vs[cur ^ 1], tid);
     }
-    if (more && ldv) tile.store_rows(Vs[cur ^ 1], li);
     __syncthreads();
   }
   if (!active) return;
@@ -345,22 +343,20 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
 // dK, dV.  grid (ceil(T/128), NH, B); each wave owns 32 keys and walks the
 // query tiles at or after them.  Per key column (one per lane):
 // P = exp(S - LSE), dV += dO^T P, dP = dO V^T, dS = P (dP - D), dK += scale Q^T dS.
-// Per query tile: Q and dO, each stored row-major and transposed; LSE and D.
+// Per query tile: Q and dO rows (their transposes come from transposing
+// reads), and the tile's LSE and D values.
 // ------------------------------------------------------------------------
 template <typename T, int HD>
 __global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
-                                                              const float* __restrict__ lse,
-                                                              const float* __restrict__ dsum, T* __restrict__ dqkv,
-                                                              int T_, int NH, float sl2, float scale) {
-  typedef BlockTile<T, HD> BT;
-  constexpr int LDK = BT::LDR, LDV = BT::LDT, ND = HD / 16, NDT = HD / 32, NB = BT::NBLK;
-  static_assert(2 * NB <= NW * 64 && KT <= NW * 64, "tile loaders must fit in the block");
+                                                           const float* __restrict__ lse, const float* __restrict__ dsum,
+                                                           T* __restrict__ dqkv, int T_, int NH, float sl2,
+                                                           float scale) {
+  typedef RowTile<T, HD> RT;
+  constexpr int LD = RT::LD, ND = HD / 16, NDT = HD / 32;
   typedef typename Frag<T>::type F;
   typedef typename Quad<T>::type Q;
-  __shared__ __attribute__((aligned(16))) T Qs[2][KT * LDK];
-  __shared__ __attribute__((aligned(16))) T Ds[2][KT * LDK];
-  __shared__ __attribute__((aligned(16))) T Qt[2][HD * LDV];
-  __shared__ __attribute__((aligned(16))) T Dt[2][HD * LDV];
+  __shared__ __attribute__((aligned(16))) T Qs[2][KT * LD];
+  __shared__ __attribute__((aligned(16))) T Ds[2][KT * LD];
   __shared__ float Ls[2][KT], Dd[2][KT];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
@@ -372,8 +368,6 @@ __global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__
   const T* base = qkv + (int64_t)b * T_ * S3;
   const T* qbase = base + h * HD;
   const T* obase = dout + (int64_t)b * T_ * C + h * HD;
-  const bool ldq = tid < NB, ldo = tid >= NB && tid < 2 * NB;
-  const int li = ldq ? tid : tid - NB;
   const bool ldl = tid < KT;  // these threads also bring the tile's LSE and D values
   const int kv = k0 + lr;
 
@@ -396,22 +390,16 @@ __global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__
 
   const int qt_begin = (kblk * NW * WQ / KT) * KT;
   const int ntiles = (T_ - qt_begin) / KT;
-  BT tile;
+  RT qt, ot;
   float sl = 0.f, sd = 0.f;
-  if (ldq) tile.load(qbase + (int64_t)qt_begin * S3, S3, li);
-  if (ldo) tile.load(obase + (int64_t)qt_begin * C, C, li);
+  qt.load(qbase + (int64_t)qt_begin * S3, S3, tid);
+  ot.load(obase + (int64_t)qt_begin * C, C, tid);
   if (ldl) {
     sl = lrow[qt_begin + tid] * LOG2E;
     sd = drow[qt_begin + tid];
   }
-  if (ldq) {
-    tile.store_rows(Qs[0], li);
-    tile.store_t(Qt[0], li);
-  }
-  if (ldo) {
-    tile.store_rows(Ds[0], li);
-    tile.store_t(Dt[0], li);
-  }
+  qt.store(Qs[0], tid);
+  ot.store(Ds[0], tid);
   if (ldl) {
     Ls[0][tid] = sl;
     Dd[0][tid] = sd;
@@ -420,13 +408,16 @@ __global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__
   for (int it = 0; it < ntiles; it++) {
     const int cur = it & 1, qt0 = qt_begin + it * KT;
     const bool more = it + 1 < ntiles;
-    if (more && ldq) tile.load(qbase + (int64_t)(qt0 + KT) * S3, S3, li);
-    if (more && ldo) tile.load(obase + (int64_t)(qt0 + KT) * C, C, li);
-    if (more && ldl) {
-      sl = lrow[qt0 + KT + tid] * LOG2E;
-      sd = drow[qt0 + KT + tid];
+    if (more) {
+      qt.load(qbase + (int64_t)(qt0 + KT) * S3, S3, tid);
+      ot.load(obase + (int64_t)(qt0 + KT) * C, C, tid);
+      if (ldl) {
+        sl = lrow[qt0 + KT + tid] * LOG2E;
+        sd = drow[qt0 + KT + tid];
+      }
     }
     if (active && qt0 + KT - 1 >= k0) {
+      const bool diag = qt0 < k0 + WQ - 1;
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int c2 = 0; c2 < 2; c2++) {
@@ -434,13 +425,14 @@ __global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__
         dp[c2] = f32x16{};
 #pragma unroll
         for (int ds = 0; ds < ND; ds++) {
-          mma16(s[c2], ld8(Qs[cur] + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), kf[ds]);
-          mma16(dp[c2], ld8(Ds[cur] + (c2 * 32 + lr) * LDK + ds * 16 + 8 * lg), vf[ds]);
+          mma16(s[c2], ld8(Qs[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), kf[ds]);
+          mma16(dp[c2], ld8(Ds[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), vf[ds]);
         }
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int ql = c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          const float p = qt0 + ql >= kv ? exp2f(s[c2][r] * sl2 - Ls[cur][ql]) : 0.f;
+          float p = fast_exp2(fmaf(s[c2][r], sl2, -Ls[cur][ql]));
+          if (diag && qt0 + ql < kv) p = 0.f;
           s[c2][r] = p;
           dp[c2][r] = p * (dp[c2][r] - Dd[cur][ql]);
         }
@@ -451,22 +443,18 @@ __global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__
         const F sf = acc_frag<T>(dp[c / 2], c % 2);
 #pragma unroll
         for (int dt = 0; dt < NDT; dt++) {
-          mma16(dv[dt], ld_split(Dt[cur], LDV, dt * 32 + lr, c, lg), pf);
-          mma16(dk[dt], ld_split(Qt[cur], LDV, dt * 32 + lr, c, lg), sf);
+          mma16(dv[dt], ld_tsplit<T, LD>(Ds[cur], dt * 32, c, lane), pf);
+          mma16(dk[dt], ld_tsplit<T, LD>(Qs[cur], dt * 32, c, lane), sf);
         }
       }
     }
-    if (more && ldq) {
-      tile.store_rows(Qs[cur ^ 1], li);
-      tile.store_t(Qt[cur ^ 1], li);
-    }
-    if (more && ldo) {
-      tile.store_rows(Ds[cur ^ 1], li);
-      tile.store_t(Dt[cur ^ 1], li);
-    }
-    if (more && ldl) {
-      Ls[cur ^ 1][tid] = sl;
-      Dd[cur ^ 1][tid] = sd;
+    if (more) {
+      qt.store(Qs[cur ^ 1], tid);
+      ot.store(Ds[cur ^ 1], tid);
+      if (ldl) {
+        Ls[cur ^ 1][tid] = sl;
+        Dd[cur ^ 1][tid] = sd;
+      }
     }
     __syncthreads();
   }
