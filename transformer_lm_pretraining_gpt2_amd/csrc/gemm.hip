@@ -96,6 +96,20 @@ struct Operand {
   }
 };
 
+// acc + the sum of a fragment's 8 values, in slot order
+__device__ __forceinline__ float frag_sum(bf16x8 f, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[e], f[e + 1]}, one, acc, false);
+  return acc;
+}
+__device__ __forceinline__ float frag_sum(f32x8 f, float acc) {
+#pragma unroll
+  for (int e = 0; e < 8; e++) acc += f[e];
+  return acc;
+}
+
 template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI>
 __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   constexpr int NT = WI * WJ * 64;
@@ -137,10 +151,21 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   _Pragma("unroll") for (int ks = 0; ks < BK / 16; ks++) {                                        \
     F fa[TI], fb[TJ];                                                                             \
     _Pragma("unroll") for (int ti = 0; ti < TI; ti++) fa[ti] = OA::frag(AS, wi * WTI + ti * 32, ks, lane); \
+    if constexpr (AT == 1 && EPI == EPI_F32) {                                                    \
+      if (do_cs) _Pragma("unroll") for (int ti = 0; ti < TI; ti++) cs[ti] = frag_sum(fa[ti], cs[ti]); \
+    }                                                                                             \
     _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) fb[tj] = OB::frag(BS, wj * WTJ + tj * 32, ks, lane); \
     _Pragma("unroll") for (int ti = 0; ti < TI; ti++)                                             \
       _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) mma16(acc[ti][tj], fb[tj], fa[ti]);       \
   }
+
+  // Bias gradient: sum_r A(i, r) from the A fragments already in registers,
+  // by the waves of the first column tile (wj == 0 of bj == 0); each lane adds
+  // its 8 reduction values per fragment in a fixed order.
+  const bool do_cs = AT == 1 && EPI == EPI_F32 && g.colsum != nullptr && bj == 0 && wj == 0;
+  float cs[TI];
+#pragma unroll
+  for (int ti = 0; ti < TI; ti++) cs[ti] = 0.f;
 
   // Two register stages: the tile two steps ahead is loaded while the current
   // one is consumed from LDS and the next one is stored to the other buffer.
@@ -182,6 +207,14 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   }
 
 #undef GEMM_COMPUTE
+  if (do_cs) {
+#pragma unroll
+    for (int ti = 0; ti < TI; ti++) {
+      const float t = cs[ti] + __shfl_xor(cs[ti], 32, 64);  // the two halves of each row's reduction values
+      const int i = i0 + wi * WTI + ti * 32 + (lane & 31);
+      if (lane < 32 && i < g.M) g.colsum[(int64_t)blockIdx.y * g.colsum_stride + i] = t;
+    }
+  }
   const int lr = lane & 31, lg = lane >> 5;
   // Epilogue: accumulator r of lane l holds out[i][j] with
   // i = tile row base + l%32, j = tile col base + 8*(r/4) + 4*(l/32) + r%4.

@@ -108,7 +108,6 @@ struct Plan {
   int64_t wpart, lnpart, cspart, normpart;
   int64_t ska, sva, skb, svb, seg, nseg;
   int64_t flags, scale, norm;
-  int cs_chunks;
   std::vector<int> split;  // split-K factor per layer weight kind (qkv, proj, fc, fcproj)
 };
 
@@ -160,8 +159,7 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
   for (int k = 0; k < 4; k++) wmax = std::max(wmax, (int64_t)P.split[k] * wsz[k]);
   P.wpart = take(4 * wmax);
   P.lnpart = take(4 * (int64_t)layernorm_bwd_parts((int)M) * 2 * C);
-  P.cs_chunks = (int)std::min<int64_t>(256, M);
-  P.cspart = take(4 * (int64_t)P.cs_chunks * 4 * C);
+  P.cspart = take(4 * (int64_t)16 * 4 * C);  // bias-gradient partials: splits (<= 16) x out width
   P.normpart = take(8 * (int64_t)grad_norm_parts());
   P.ska = take(4 * M);
   P.sva = take(4 * M);
@@ -314,10 +312,11 @@ GemmArgs dx_args(gpt2_t* h, const void* dY, const void* W, int N, int K, void* o
   return g;
 }
 
-// Weight gradient of W [N, K]: dW (+)= dY^T X, dY [M, N], X [M, K]; split-K
-// partials are reduced in order into the gradient buffer.
-int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* dW, int splits, int accumulate,
-                const char* what) {
+// Weight gradient of W [N, K]: dW (+)= dY^T X, dY [M, N], X [M, K], and the
+// bias gradient db (+)= sum_rows dY (column sums fused into the same product);
+// split-K partials are reduced in order into the gradient buffers.
+int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* dW, float* db, int splits,
+                int accumulate, const char* what) {
   GemmArgs g;
   g.A = dY;
   g.lda = N;
@@ -327,26 +326,27 @@ int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* d
   g.N = K;
   g.K = (int)h->M;
   g.splits = splits;
+  float* cpart = h->w<float>(h->plan.cspart);
+  if (db) {
+    g.colsum = cpart;
+    g.colsum_stride = N;
+  }
+  int rc;
   if (splits == 1) {
     g.C = dW;
     g.ldc = K;
     g.accumulate = accumulate;
-    return run_gemm(h, K_GEMM_TN_F32, 1, 1, EPI_F32, g, what);
+    rc = run_gemm(h, K_GEMM_TN_F32, 1, 1, EPI_F32, g, what);
+  } else {
+    float* part = h->w<float>(h->plan.wpart);
+    g.C = part;
+    g.ldc = K;
+    g.split_stride = (int64_t)N * K;
+    rc = run_gemm(h, K_GEMM_TN_F32, 1, 1, EPI_F32, g, what);
+    if (!rc) rc = hip_check(h, reduce_parts(h->st, part, splits, (int64_t)N * K, dW, N * K, accumulate), "reduce dW");
   }
-  float* part = h->w<float>(h->plan.wpart);
-  g.C = part;
-  g.ldc = K;
-  g.split_stride = (int64_t)N * K;
-  int rc = run_gemm(h, K_GEMM_TN_F32, 1, 1, EPI_F32, g, what);
-  if (rc) return rc;
-  return hip_check(h, reduce_parts(h->st, part, splits, (int64_t)N * K, dW, N * K, accumulate), "reduce dW");
-}
-
-int bias_grad(gpt2_t* h, const void* dY, int x_is_f32, int N, float* db, int accumulate) {
-  float* part = h->w<float>(h->plan.cspart);
-  int rc = hip_check(h, colsum_parts(h->st, h->prec, x_is_f32, dY, (int)h->M, N, part, h->plan.cs_chunks), "colsum");
-  if (rc) return rc;
-  return hip_check(h, reduce_parts(h->st, part, h->plan.cs_chunks, N, db, N, accumulate), "reduce db");
+  if (!rc && db) rc = hip_check(h, reduce_parts(h->st, cpart, splits, N, db, N, accumulate), "reduce db");
+  return rc;
 }
 
 int ln_backward(gpt2_t* h, const void* dy, const float* x, const float* mean, const float* rstd, int kind_g, int layer,
@@ -600,17 +600,16 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
 
   for (int l = L - 1; l >= 0; l--) {
     // MLP down-projection: dres is the gradient of the block output
-    if ((rc = bias_grad(h, dres, 1, C, h->G32(T_FCPB, l), acc))) return rc;
-    if ((rc = weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), P.split[3], acc, "fcproj dw")))
+    if ((rc = weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), P.split[3],
+                          acc, "fcproj dw")))
       return rc;
     g = dx_args(h, dres_op, h->W(T_FCPW, l), C, 4 * C, h->w<void>(P.du));
     g.aux = h->w<void>(P.u[l]);
     g.ldaux = 4 * C;
     if ((rc = run_gemm(h, K_GEMM_NN_GELU_BWD, 0, 1, EPI_GELU_BWD, g, "fcproj dx"))) return rc;
     // MLP up-projection
-    if ((rc = bias_grad(h, h->w<void>(P.du), 0, 4 * C, h->G32(T_FCB, l), acc))) return rc;
-    if ((rc = weight_grad(h, h->w<void>(P.du), h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), P.split[2], acc,
-                          "fc dw")))
+    if ((rc = weight_grad(h, h->w<void>(P.du), h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), h->G32(T_FCB, l),
+                          P.split[2], acc, "fc dw")))
       return rc;
     g = dx_args(h, h->w<void>(P.du), h->W(T_FCW, l), 4 * C, C, h->w<void>(P.dh));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "fc dx"))) return rc;
@@ -618,8 +617,8 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
                           T_LN2G, l, 1, acc)))
       return rc;
     // attention output projection
-    if ((rc = bias_grad(h, dres, 1, C, h->G32(T_PROJB, l), acc))) return rc;
-    if ((rc = weight_grad(h, dres_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), P.split[1], acc, "proj dw")))
+    if ((rc = weight_grad(h, dres_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l), P.split[1],
+                          acc, "proj dw")))
       return rc;
     g = dx_args(h, dres_op, h->W(T_PROJW, l), C, C, h->w<void>(P.datty));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "proj dx"))) return rc;
@@ -646,9 +645,8 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
       if (rc) return rc;
     }
     // qkv projection
-    if ((rc = bias_grad(h, h->w<void>(P.dqkv), 0, 3 * C, h->G32(T_QKVB, l), acc))) return rc;
-    if ((rc = weight_grad(h, h->w<void>(P.dqkv), h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l), P.split[0], acc,
-                          "qkv dw")))
+    if ((rc = weight_grad(h, h->w<void>(P.dqkv), h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l), h->G32(T_QKVB, l),
+                          P.split[0], acc, "qkv dw")))
       return rc;
     g = dx_args(h, h->w<void>(P.dqkv), h->W(T_QKVW, l), 3 * C, C, h->w<void>(P.dh));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "qkv dx"))) return rc;

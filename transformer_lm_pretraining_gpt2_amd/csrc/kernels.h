@@ -34,6 +34,11 @@ struct GemmArgs {
   int splits = 1;
   int64_t split_stride = 0;
   float alpha = 1.f;  // EPI_STORE / EPI_F32: acc is scaled by alpha before the bias / accumulation
+  // EPI_F32 with a_t = 1 only: when set, the blocks of the first column tile also
+  // write sum_r A(i, r) over their reduction range to colsum[split*colsum_stride + i]
+  // (the bias gradient of a weight-gradient product, before the split reduction)
+  float* colsum = nullptr;
+  int64_t colsum_stride = 0;
 };
 
 hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArgs& g);

@@ -15,8 +15,6 @@
 namespace gpt2k {
 namespace {
 
-constexpr int MAXP = 16;  // float pairs per lane: rows of up to 64*2*16 = 2048 elements
-
 template <typename T> struct Pair;
 template <> struct Pair<bf16> { typedef bf16 __attribute__((ext_vector_type(2))) type; };
 template <> struct Pair<float> { typedef float __attribute__((ext_vector_type(2))) type; };
@@ -25,47 +23,44 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 // LayerNorm forward: one wave per row; mean and biased variance over C,
 // y = (x - mean) * rstd * g + b, rstd = 1/sqrt(var + 1e-5).
-// Lane l holds elements 2l + 128k, 2l + 128k + 1.
+// Lane l holds elements 2l + 128k, 2l + 128k + 1 (k < NP = C/128).
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int NP>
 __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ g,
                                                      const float* __restrict__ b, T* __restrict__ y,
-                                                     float* __restrict__ mean, float* __restrict__ rstd, int M, int C) {
+                                                     float* __restrict__ mean, float* __restrict__ rstd, int M) {
   typedef typename Pair<T>::type P;
+  constexpr int C = NP * 128;
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
-  const int np = C / 128;
   const float* xr = x + (int64_t)row * C;
-  f32x2 v[MAXP];
+  f32x2 v[NP];
   float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < MAXP; k++)
-    if (k < np) {
-      v[k] = *reinterpret_cast<const f32x2*>(xr + 2 * lane + 128 * k);
-      s += v[k][0] + v[k][1];
-    }
-  const float mu = wave_sum(s) / C;
+  for (int k = 0; k < NP; k++) {
+    v[k] = *reinterpret_cast<const f32x2*>(xr + 2 * lane + 128 * k);
+    s += v[k][0] + v[k][1];
+  }
+  const float mu = wave_sum(s) * (1.f / C);
   float q = 0.f;
 #pragma unroll
-  for (int k = 0; k < MAXP; k++)
-    if (k < np) {
-      const float a = v[k][0] - mu, c = v[k][1] - mu;
-      q += a * a + c * c;
-    }
-  const float rs = 1.f / sqrtf(wave_sum(q) / C + 1e-5f);
+  for (int k = 0; k < NP; k++) {
+    const float a = v[k][0] - mu, c = v[k][1] - mu;
+    q += a * a + c * c;
+  }
+  const float rs = 1.f / sqrtf(wave_sum(q) * (1.f / C) + 1e-5f);
   T* yr = y + (int64_t)row * C;
 #pragma unroll
-  for (int k = 0; k < MAXP; k++)
-    if (k < np) {
-      const int c0 = 2 * lane + 128 * k;
-      const f32x2 gg = *reinterpret_cast<const f32x2*>(g + c0);
-      const f32x2 bb = *reinterpret_cast<const f32x2*>(b + c0);
-      P o;
-      o[0] = from_f<T>((v[k][0] - mu) * rs * gg[0] + bb[0]);
-      o[1] = from_f<T>((v[k][1] - mu) * rs * gg[1] + bb[1]);
-      *reinterpret_cast<P*>(yr + c0) = o;
-    }
+  for (int k = 0; k < NP; k++) {
+    const int c0 = 2 * lane + 128 * k;
+    const f32x2 gg = *reinterpret_cast<const f32x2*>(g + c0);
+    const f32x2 bb = *reinterpret_cast<const f32x2*>(b + c0);
+    P o;
+    o[0] = from_f<T>((v[k][0] - mu) * rs * gg[0] + bb[0]);
+    o[1] = from_f<T>((v[k][1] - mu) * rs * gg[1] + bb[1]);
+    *reinterpret_cast<P*>(yr + c0) = o;
+  }
   if (lane == 0) {
     mean[row] = mu;
     rstd[row] = rs;
@@ -78,84 +73,104 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* __restrict__ x
 //   dx = rstd (d - mean_c(d) - xhat mean_c(d xhat));  dres = [dres +] dx
 // dgamma = sum_rows dy xhat, dbeta = sum_rows dy: each block writes its
 // partial sums (rows visited in a fixed order) to part[block][0:C | C:2C].
+// Each wave walks its rows with the next row's inputs already in flight.
 // ---------------------------------------------------------------------------
 constexpr int LNB_BLOCKS = 512;
 
-template <typename T>
+template <typename T, int NP>
+struct LnRow {
+  typedef typename Pair<T>::type P;
+  P dy[NP];
+  f32x2 x[NP], r[NP];
+  float mu, rs;
+  __device__ __forceinline__ void load(const T* dyp, const float* xp, const float* rp, const float* mean,
+                                       const float* rstd, int row, int lane, int accumulate) {
+    constexpr int C = NP * 128;
+#pragma unroll
+    for (int k = 0; k < NP; k++) {
+      const int c0 = 2 * lane + 128 * k;
+      dy[k] = *reinterpret_cast<const P*>(dyp + (int64_t)row * C + c0);
+      x[k] = *reinterpret_cast<const f32x2*>(xp + (int64_t)row * C + c0);
+      if (accumulate) r[k] = *reinterpret_cast<const f32x2*>(rp + (int64_t)row * C + c0);
+    }
+    mu = mean[row];
+    rs = rstd[row];
+  }
+};
+
+template <typename T, int NP>
 __global__ void __launch_bounds__(256) ln_bwd_kernel(const T* __restrict__ dy, const float* __restrict__ x,
                                                      const float* __restrict__ mean, const float* __restrict__ rstd,
                                                      const float* __restrict__ g, float* __restrict__ dres,
                                                      T* __restrict__ dres_lp, int accumulate, float* __restrict__ part,
-                                                     int M, int C) {
+                                                     int M) {
   typedef typename Pair<T>::type P;
-  extern __shared__ float sh[];  // [4 waves][2C]
+  constexpr int C = NP * 128;
+  __shared__ float sh[4][2 * C];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int np = C / 128;
-  f32x2 gg[MAXP], ag[MAXP], ab[MAXP];
+  f32x2 gg[NP], ag[NP], ab[NP];
 #pragma unroll
-  for (int k = 0; k < MAXP; k++)
-    if (k < np) {
-      gg[k] = *reinterpret_cast<const f32x2*>(g + 2 * lane + 128 * k);
-      ag[k] = f32x2{0.f, 0.f};
-      ab[k] = f32x2{0.f, 0.f};
-    }
-  for (int row = blockIdx.x * 4 + w; row < M; row += gridDim.x * 4) {
-    const float mu = mean[row], rs = rstd[row];
-    const T* dyr = dy + (int64_t)row * C;
-    const float* xr = x + (int64_t)row * C;
-    f32x2 xh[MAXP], d[MAXP];
+  for (int k = 0; k < NP; k++) {
+    gg[k] = *reinterpret_cast<const f32x2*>(g + 2 * lane + 128 * k);
+    ag[k] = f32x2{0.f, 0.f};
+    ab[k] = f32x2{0.f, 0.f};
+  }
+  const int stride = gridDim.x * 4;
+  int row = blockIdx.x * 4 + w;
+  LnRow<T, NP> cur;
+  if (row < M) cur.load(dy, x, dres, mean, rstd, row, lane, accumulate);
+  while (row < M) {
+    const int next = row + stride;
+    LnRow<T, NP> nxt;
+    if (next < M) nxt.load(dy, x, dres, mean, rstd, next, lane, accumulate);
+    f32x2 xh[NP], d[NP];
     float sd = 0.f, sdx = 0.f;
 #pragma unroll
-    for (int k = 0; k < MAXP; k++)
-      if (k < np) {
-        const int c0 = 2 * lane + 128 * k;
-        const P dv = *reinterpret_cast<const P*>(dyr + c0);
-        const f32x2 xv = *reinterpret_cast<const f32x2*>(xr + c0);
-        const float d0 = to_f<T>(dv[0]), d1 = to_f<T>(dv[1]);
-        xh[k] = f32x2{(xv[0] - mu) * rs, (xv[1] - mu) * rs};
-        ag[k][0] += d0 * xh[k][0];
-        ag[k][1] += d1 * xh[k][1];
-        ab[k][0] += d0;
-        ab[k][1] += d1;
-        d[k] = f32x2{d0 * gg[k][0], d1 * gg[k][1]};
-        sd += d[k][0] + d[k][1];
-        sdx += d[k][0] * xh[k][0] + d[k][1] * xh[k][1];
-      }
-    sd = wave_sum(sd) / C;
-    sdx = wave_sum(sdx) / C;
+    for (int k = 0; k < NP; k++) {
+      const float d0 = to_f<T>(cur.dy[k][0]), d1 = to_f<T>(cur.dy[k][1]);
+      xh[k] = f32x2{(cur.x[k][0] - cur.mu) * cur.rs, (cur.x[k][1] - cur.mu) * cur.rs};
+      ag[k][0] += d0 * xh[k][0];
+      ag[k][1] += d1 * xh[k][1];
+      ab[k][0] += d0;
+      ab[k][1] += d1;
+      d[k] = f32x2{d0 * gg[k][0], d1 * gg[k][1]};
+      sd += d[k][0] + d[k][1];
+      sdx += d[k][0] * xh[k][0] + d[k][1] * xh[k][1];
+    }
+    sd = wave_sum(sd) * (1.f / C);
+    sdx = wave_sum(sdx) * (1.f / C);
     float* rr = dres + (int64_t)row * C;
 #pragma unroll
-    for (int k = 0; k < MAXP; k++)
-      if (k < np) {
-        const int c0 = 2 * lane + 128 * k;
-        f32x2 o{rs * (d[k][0] - sd - xh[k][0] * sdx), rs * (d[k][1] - sd - xh[k][1] * sdx)};
-        if (accumulate) {
-          const f32x2 prev = *reinterpret_cast<const f32x2*>(rr + c0);
-          o[0] += prev[0];
-          o[1] += prev[1];
-        }
-        *reinterpret_cast<f32x2*>(rr + c0) = o;
-        if (dres_lp) {
-          P lp;
-          lp[0] = from_f<T>(o[0]);
-          lp[1] = from_f<T>(o[1]);
-          *reinterpret_cast<P*>(dres_lp + (int64_t)row * C + c0) = lp;
-        }
+    for (int k = 0; k < NP; k++) {
+      const int c0 = 2 * lane + 128 * k;
+      f32x2 o{cur.rs * (d[k][0] - sd - xh[k][0] * sdx), cur.rs * (d[k][1] - sd - xh[k][1] * sdx)};
+      if (accumulate) {
+        o[0] += cur.r[k][0];
+        o[1] += cur.r[k][1];
       }
+      *reinterpret_cast<f32x2*>(rr + c0) = o;
+      if (dres_lp) {
+        P lp;
+        lp[0] = from_f<T>(o[0]);
+        lp[1] = from_f<T>(o[1]);
+        *reinterpret_cast<P*>(dres_lp + (int64_t)row * C + c0) = lp;
+      }
+    }
+    cur = nxt;
+    row = next;
   }
   // block partials: waves combined in index order
 #pragma unroll
-  for (int k = 0; k < MAXP; k++)
-    if (k < np) {
-      const int c0 = 2 * lane + 128 * k;
-      sh[w * 2 * C + c0] = ag[k][0];
-      sh[w * 2 * C + c0 + 1] = ag[k][1];
-      sh[w * 2 * C + C + c0] = ab[k][0];
-      sh[w * 2 * C + C + c0 + 1] = ab[k][1];
-    }
+  for (int k = 0; k < NP; k++) {
+    const int c0 = 2 * lane + 128 * k;
+    sh[w][c0] = ag[k][0];
+    sh[w][c0 + 1] = ag[k][1];
+    sh[w][C + c0] = ab[k][0];
+    sh[w][C + c0 + 1] = ab[k][1];
+  }
   __syncthreads();
   for (int j = threadIdx.x; j < 2 * C; j += 256)
-    part[(int64_t)blockIdx.x * 2 * C + j] = ((sh[j] + sh[2 * C + j]) + sh[4 * C + j]) + sh[6 * C + j];
+    part[(int64_t)blockIdx.x * 2 * C + j] = ((sh[0][j] + sh[1][j]) + sh[2][j]) + sh[3][j];
 }
 
 // out[j] = [out[j] +] sum_p part[p*ld + j].  A block of 16 waves covers 256
@@ -577,14 +592,30 @@ __global__ void to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+#define LN_NP_DISPATCH(C, F)       \
+  switch ((C) / 128) {              \
+    case 1: F(1); break;            \
+    case 2: F(2); break;            \
+    case 3: F(3); break;            \
+    case 4: F(4); break;            \
+    case 6: F(6); break;            \
+    case 8: F(8); break;            \
+    case 12: F(12); break;          \
+    case 16: F(16); break;          \
+    default: return hipErrorInvalidValue; \
+  }
+
 hipError_t layernorm_fwd(hipStream_t st, Prec p, const float* x, const float* g, const float* b, void* y, float* mean,
                          float* rstd, int M, int C) {
-  if (C % 128 != 0 || C > 128 * MAXP) return hipErrorInvalidValue;
+  if (C % 128 != 0) return hipErrorInvalidValue;
   dim3 grid((M + 3) / 4);
-  if (p == BF16)
-    hipLaunchKernelGGL(ln_fwd_kernel<bf16>, grid, dim3(256), 0, st, x, g, b, static_cast<bf16*>(y), mean, rstd, M, C);
-  else
-    hipLaunchKernelGGL(ln_fwd_kernel<float>, grid, dim3(256), 0, st, x, g, b, static_cast<float*>(y), mean, rstd, M, C);
+#define LNF(NP)                                                                                                    \
+  if (p == BF16)                                                                                                   \
+    hipLaunchKernelGGL((ln_fwd_kernel<bf16, NP>), grid, dim3(256), 0, st, x, g, b, static_cast<bf16*>(y), mean, rstd, M); \
+  else                                                                                                             \
+    hipLaunchKernelGGL((ln_fwd_kernel<float, NP>), grid, dim3(256), 0, st, x, g, b, static_cast<float*>(y), mean, rstd, M);
+  LN_NP_DISPATCH(C, LNF)
+#undef LNF
   return hipGetLastError();
 }
 
@@ -593,16 +624,18 @@ int layernorm_bwd_parts(int M) { return std::min(LNB_BLOCKS, (M + 3) / 4); }
 hipError_t layernorm_bwd(hipStream_t st, Prec p, const void* dy, const float* x, const float* mean, const float* rstd,
                          const float* g, float* dres, void* dres_lp, int accumulate, float* part, int M, int C,
                          int* nparts) {
-  if (C % 128 != 0 || C > 128 * MAXP) return hipErrorInvalidValue;
+  if (C % 128 != 0) return hipErrorInvalidValue;
   const int nb = layernorm_bwd_parts(M);
   *nparts = nb;
-  const size_t shm = 4 * 2 * C * sizeof(float);
-  if (p == BF16)
-    hipLaunchKernelGGL(ln_bwd_kernel<bf16>, dim3(nb), dim3(256), shm, st, static_cast<const bf16*>(dy), x, mean, rstd, g,
-                       dres, static_cast<bf16*>(dres_lp), accumulate, part, M, C);
-  else
-    hipLaunchKernelGGL(ln_bwd_kernel<float>, dim3(nb), dim3(256), shm, st, static_cast<const float*>(dy), x, mean, rstd,
-                       g, dres, static_cast<float*>(dres_lp), accumulate, part, M, C);
+#define LNB(NP)                                                                                                     \
+  if (p == BF16)                                                                                                    \
+    hipLaunchKernelGGL((ln_bwd_kernel<bf16, NP>), dim3(nb), dim3(256), 0, st, static_cast<const bf16*>(dy), x, mean, \
+                       rstd, g, dres, static_cast<bf16*>(dres_lp), accumulate, part, M);                            \
+  else                                                                                                              \
+    hipLaunchKernelGGL((ln_bwd_kernel<float, NP>), dim3(nb), dim3(256), 0, st, static_cast<const float*>(dy), x,    \
+                       mean, rstd, g, dres, static_cast<float*>(dres_lp), accumulate, part, M);
+  LN_NP_DISPATCH(C, LNB)
+#undef LNB
   return hipGetLastError();
 }
 
