@@ -40,8 +40,9 @@ def kernel_source_hash():
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None
-    when they are missing or were taken on a different kernel source."""
+    """HBM bytes per launch (fetched + written) from the committed rocprofv3
+    counter runs, or None when they are missing or were taken on a different
+    kernel source (see transformer_lm_pretraining_gpt2_amd/traffic.py)."""
     try:
         with open(TRAFFIC_FILE) as fh:
             d = json.load(fh)
@@ -89,6 +90,8 @@ def main():
     ap.add_argument("--roofline-kernel", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="before warmup, one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -138,6 +141,14 @@ def main():
         step.adamw_step(s + 1, lr_at(s, rc.max_lr, rc.warmup, rc.max_steps), rc.beta1, rc.beta2, rc.eps,
                         rc.weight_decay, rc.grad_clip, norm)
 
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for s in range(W):
         one_step(s)
     st = step.sync_status()

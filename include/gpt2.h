@@ -175,7 +175,8 @@ const char* gpt2_strerror(int code);
 
 /* Number of timeable kernels, and the name of kernel id in [0, count):
  * gemm_nt_store, gemm_nt_gelu, gemm_nt_resid, gemm_nn_store, gemm_nn_gelu_bwd,
- * gemm_tn_f32, attn_fwd, attn_bwd_dkv, attn_bwd_dq, cross_entropy,
+ * gemm_tn_f32 (per-layer weight gradients), gemm_tn_lmhead (weight gradient of
+ * the tied output layer), attn_fwd, attn_bwd_dkv, attn_bwd_dq, cross_entropy,
  * layernorm_fwd, layernorm_bwd, adamw.  NULL for an invalid id. */
 int gpt2_kernel_count(void);
 const char* gpt2_kernel_name(int kernel_id);

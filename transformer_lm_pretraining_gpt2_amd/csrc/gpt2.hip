@@ -258,6 +258,7 @@ enum {
   K_GEMM_NN_STORE,
   K_GEMM_NN_GELU_BWD,
   K_GEMM_TN_F32,
+  K_GEMM_TN_LMHEAD,
   K_ATTN_FWD,
   K_ATTN_DKV,
   K_ATTN_DQ,
@@ -269,7 +270,7 @@ enum {
 };
 static const char* const kKernelNames[K_COUNT] = {
     "gemm_nt_store", "gemm_nt_gelu", "gemm_nt_resid", "gemm_nn_store", "gemm_nn_gelu_bwd", "gemm_tn_f32",
-    "attn_fwd",      "attn_bwd_dkv", "attn_bwd_dq",   "cross_entropy", "layernorm_fwd",     "layernorm_bwd",
+    "gemm_tn_lmhead", "attn_fwd",      "attn_bwd_dkv", "attn_bwd_dq",   "cross_entropy", "layernorm_fwd",     "layernorm_bwd",
     "adamw"};
 
 namespace {
@@ -592,7 +593,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     w.ldc = C;
     w.accumulate = acc;
     w.alpha = alpha;
-    if ((rc = run_gemm(h, K_GEMM_TN_F32, 1, 1, EPI_F32, w, "lm_head dw"))) return rc;
+    if ((rc = run_gemm(h, K_GEMM_TN_LMHEAD, 1, 1, EPI_F32, w, "lm_head dw"))) return rc;
   }
   if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[L]), h->w<float>(P.meanf), h->w<float>(P.rstdf), T_LNFG,
                         -1, 0, acc)))
