@@ -64,15 +64,19 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // tanh-approximate GELU and its derivative ("Karpathy's four-hour GPT-2
 // reproduction in one post", what I checked myself: GPT-2 uses the tanh form).
-__device__ __forceinline__ float gelu_tanh(float x) {
-  const float k = 0.7978845608028654f;  // sqrt(2/pi)
-  float t = tanhf(k * (x + 0.044715f * x * x * x));
-  return 0.5f * x * (1.0f + t);
+// With z = 2*sqrt(2/pi)*(x + 0.044715 x^3), 0.5*(1 + tanh(z/2)) = sigmoid(z), so
+// gelu(x) = x * s and gelu'(x) = s + x * s * (1 - s) * dz/dx, s = sigmoid(z);
+// sigmoid is evaluated with the hardware exp2 and reciprocal.
+__device__ __forceinline__ float gelu_sigmoid(float x) {
+  const float k2 = 2.f * 0.7978845608028654f * 1.4426950408889634f;  // 2*sqrt(2/pi)*log2(e)
+  const float z2 = k2 * x * (1.f + 0.044715f * x * x);               // z * log2(e)
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z2));
 }
+__device__ __forceinline__ float gelu_tanh(float x) { return x * gelu_sigmoid(x); }
 __device__ __forceinline__ float gelu_tanh_grad(float x) {
-  const float k = 0.7978845608028654f;
-  float t = tanhf(k * (x + 0.044715f * x * x * x));
-  return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * k * (1.0f + 3.0f * 0.044715f * x * x);
+  const float k = 2.f * 0.7978845608028654f;
+  const float s = gelu_sigmoid(x);
+  return s + x * s * (1.f - s) * k * (1.f + 3.f * 0.044715f * x * x);
 }
 
 // Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).

@@ -119,8 +119,15 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   typedef Operand<T, BN, BK, NT, BT> OB;
   typedef typename Frag<T>::type F;
   typedef typename Quad<T>::type Q;
-  __shared__ __attribute__((aligned(16))) T sA[2][OA::ELEMS];
-  __shared__ __attribute__((aligned(16))) T sB[2][OB::ELEMS];
+  // Operand tiles (two buffers each) and, after the main loop, the epilogue's
+  // staging area for half of the output tile (fp32) share one LDS block.
+  constexpr int RP = BM / WI;                 // output rows staged per pass (one row of waves)
+  constexpr int SLD = BN + 4;                 // staging row length (floats)
+  constexpr int OPER_BYTES = 2 * (OA::ELEMS + OB::ELEMS) * (int)sizeof(T);
+  constexpr int STAGE_BYTES = RP * SLD * 4;
+  __shared__ __attribute__((aligned(16))) char smem[OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES];
+  T (*sA)[OA::ELEMS] = reinterpret_cast<T (*)[OA::ELEMS]>(smem);
+  T (*sB)[OB::ELEMS] = reinterpret_cast<T (*)[OB::ELEMS]>(smem + 2 * OA::ELEMS * sizeof(T));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wi = wave / WJ, wj = wave % WJ;
@@ -216,72 +223,66 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
     }
   }
   const int lr = lane & 31, lg = lane >> 5;
-  // Epilogue: accumulator r of lane l holds out[i][j] with
-  // i = tile row base + l%32, j = tile col base + 8*(r/4) + 4*(l/32) + r%4.
+  // Epilogue, staged through LDS one row of waves at a time so every global
+  // access is a coalesced 16-byte run along an output row.  Accumulator r of
+  // lane l holds out[i][j] with i = tile row base + l%32 and
+  // j = tile col base + 8*(r/4) + 4*(l/32) + r%4.
+  float* stage = reinterpret_cast<float*>(smem);
+  constexpr int CPRW = BN / 8;  // 8-column chunks per staged row
+#pragma unroll 1
+  for (int pass = 0; pass < WI; pass++) {
+    __syncthreads();  // operand tiles (or the previous pass) are no longer read
+    if (wi == pass) {
 #pragma unroll
-  for (int ti = 0; ti < TI; ti++) {
-    const int i = i0 + wi * WTI + ti * 32 + lr;
-    if (i >= g.M) continue;
+      for (int ti = 0; ti < TI; ti++)
 #pragma unroll
-    for (int tj = 0; tj < TJ; tj++) {
+        for (int tj = 0; tj < TJ; tj++)
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int j = j0 + wj * WTJ + tj * 32 + 8 * q + 4 * lg;
-        if (j >= g.N) continue;
-        float v[4];
+          for (int q = 0; q < 4; q++) {
+            const int il = ti * 32 + lr, jl = wj * WTJ + tj * 32 + 8 * q + 4 * lg;
+            *reinterpret_cast<f32x4*>(stage + il * SLD + jl) =
+                f32x4{acc[ti][tj][4 * q], acc[ti][tj][4 * q + 1], acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]};
+          }
+    }
+    __syncthreads();
+    for (int c = tid; c < RP * CPRW; c += NT) {
+      const int il = c / CPRW, jl = (c % CPRW) * 8;
+      const int i = i0 + pass * RP + il, j = j0 + jl;
+      if (i >= g.M || j >= g.N) continue;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl + 4);
+      f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if constexpr (EPI == EPI_STORE || EPI == EPI_F32) v *= g.alpha;
+      if constexpr (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID) {
+        if (EPI != EPI_STORE || g.bias) v += ld8(g.bias + j);
+      }
+      if constexpr (EPI == EPI_STORE) {
+        F o;
 #pragma unroll
-        for (int e = 0; e < 4; e++) v[e] = acc[ti][tj][4 * q + e];
-        if constexpr (EPI == EPI_STORE || EPI == EPI_F32) {
+        for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e]);
+        st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
+      } else if constexpr (EPI == EPI_GELU) {
+        F u, o;
 #pragma unroll
-          for (int e = 0; e < 4; e++) v[e] *= g.alpha;
+        for (int e = 0; e < 8; e++) {
+          u[e] = from_f<T>(v[e]);
+          o[e] = from_f<T>(gelu_tanh(v[e]));
         }
-        if constexpr (EPI == EPI_STORE) {
-          if (g.bias) {
-            const f32x4 b = *reinterpret_cast<const f32x4*>(g.bias + j);
+        st8(static_cast<T*>(g.aux) + (int64_t)i * g.ldaux + j, u);
+        st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
+      } else if constexpr (EPI == EPI_RESID) {
+        v += ld8(g.resid + (int64_t)i * g.ldr + j);
+        st8(static_cast<float*>(g.C) + (int64_t)i * g.ldc + j, v);
+      } else if constexpr (EPI == EPI_GELU_BWD) {
+        const F u = ld8(static_cast<const T*>(g.aux) + (int64_t)i * g.ldaux + j);
+        F o;
 #pragma unroll
-            for (int e = 0; e < 4; e++) v[e] += b[e];
-          }
-          Q o;
-#pragma unroll
-          for (int e = 0; e < 4; e++) o[e] = from_f<T>(v[e]);
-          *reinterpret_cast<Q*>(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j) = o;
-        } else if constexpr (EPI == EPI_GELU) {
-          const f32x4 b = *reinterpret_cast<const f32x4*>(g.bias + j);
-          Q u, o;
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const float x = v[e] + b[e];
-            u[e] = from_f<T>(x);
-            o[e] = from_f<T>(gelu_tanh(x));
-          }
-          *reinterpret_cast<Q*>(static_cast<T*>(g.aux) + (int64_t)i * g.ldaux + j) = u;
-          *reinterpret_cast<Q*>(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j) = o;
-        } else if constexpr (EPI == EPI_RESID) {
-          const f32x4 b = *reinterpret_cast<const f32x4*>(g.bias + j);
-          const f32x4 r = *reinterpret_cast<const f32x4*>(g.resid + (int64_t)i * g.ldr + j);
-          f32x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; e++) o[e] = r[e] + (v[e] + b[e]);
-          *reinterpret_cast<f32x4*>(static_cast<float*>(g.C) + (int64_t)i * g.ldc + j) = o;
-        } else if constexpr (EPI == EPI_GELU_BWD) {
-          const Q u = *reinterpret_cast<const Q*>(static_cast<const T*>(g.aux) + (int64_t)i * g.ldaux + j);
-          Q o;
-#pragma unroll
-          for (int e = 0; e < 4; e++) o[e] = from_f<T>(v[e] * gelu_tanh_grad(to_f<T>(u[e])));
-          *reinterpret_cast<Q*>(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j) = o;
-        } else {  // EPI_F32
-          float* C = static_cast<float*>(g.C) + (int64_t)blockIdx.y * g.split_stride + (int64_t)i * g.ldc + j;
-          f32x4 o;
-          if (g.accumulate) {
-            const f32x4 c = *reinterpret_cast<const f32x4*>(C);
-#pragma unroll
-            for (int e = 0; e < 4; e++) o[e] = c[e] + v[e];
-          } else {
-#pragma unroll
-            for (int e = 0; e < 4; e++) o[e] = v[e];
-          }
-          *reinterpret_cast<f32x4*>(C) = o;
-        }
+        for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e] * gelu_tanh_grad(to_f<T>(u[e])));
+        st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
+      } else {  // EPI_F32
+        float* Cp = static_cast<float*>(g.C) + (int64_t)blockIdx.y * g.split_stride + (int64_t)i * g.ldc + j;
+        if (g.accumulate) v += ld8(Cp);
+        st8(Cp, v);
       }
     }
   }
