@@ -110,6 +110,12 @@ __device__ __forceinline__ float frag_sum(f32x8 f, float acc) {
   return acc;
 }
 
+// Which instantiations can produce the bias gradient: weight-gradient products
+// (strided A, fp32 output) on 4-wave tiles.  The 8-wave tile serves only the
+// bias-free tied output layer; a second copy of its main loop would not fit
+// its 256 registers.
+constexpr bool gemm_has_colsum(int at, int epi, int waves) { return at == 1 && epi == EPI_F32 && waves == 4; }
+
 template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI>
 __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   constexpr int NT = WI * WJ * 64;
@@ -154,67 +160,95 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int tj = 0; tj < TJ; tj++) acc[ti][tj] = f32x16{};
 
-#define GEMM_COMPUTE(AS, BS)                                                                      \
-  _Pragma("unroll") for (int ks = 0; ks < BK / 16; ks++) {                                        \
-    F fa[TI], fb[TJ];                                                                             \
-    _Pragma("unroll") for (int ti = 0; ti < TI; ti++) fa[ti] = OA::frag(AS, wi * WTI + ti * 32, ks, lane); \
-    if constexpr (AT == 1 && EPI == EPI_F32) {                                                    \
-      if (do_cs) _Pragma("unroll") for (int ti = 0; ti < TI; ti++) cs[ti] = frag_sum(fa[ti], cs[ti]); \
+  // One LDS tile: BK/16 substeps of TI x TJ MFMAs.  With PIPE the fragments
+  // of substep ks+1 are read before the MFMAs of substep ks are issued, so LDS
+  // latency overlaps the matrix core (a gain when both operands come from
+  // plain LDS rows; with two transposed operands the extra registers cost
+  // more than the overlap wins).  CSV = 1 also accumulates the bias gradient
+  // sum_r A(i, r) from the A fragments: each lane adds its 8 reduction values
+  // per fragment in a fixed order.
+  constexpr bool PIPE = AT == 0;
+  constexpr bool HAS_CS = gemm_has_colsum(AT, EPI, WI * WJ);
+#define GEMM_FRAGS(AS, BS, KS, FA, FB)                                                            \
+  _Pragma("unroll") for (int ti = 0; ti < TI; ti++) FA[ti] = OA::frag(AS, wi * WTI + ti * 32, KS, lane); \
+  _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) FB[tj] = OB::frag(BS, wj * WTJ + tj * 32, KS, lane);
+#define GEMM_COMPUTE(AS, BS, CSV)                                                                 \
+  {                                                                                               \
+    F fa[2][TI], fb[2][TJ];                                                                       \
+    if constexpr (PIPE) { GEMM_FRAGS(AS, BS, 0, fa[0], fb[0]) }                                   \
+    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ks++) {                                      \
+      const int cur = PIPE ? ks & 1 : 0;                                                          \
+      if constexpr (PIPE) {                                                                       \
+        if (ks + 1 < BK / 16) { GEMM_FRAGS(AS, BS, ks + 1, fa[cur ^ 1], fb[cur ^ 1]) }            \
+      } else {                                                                                    \
+        GEMM_FRAGS(AS, BS, ks, fa[0], fb[0])                                                      \
+      }                                                                                           \
+      if constexpr (CSV) {                                                                        \
+        _Pragma("unroll") for (int ti = 0; ti < TI; ti++) cs[ti] = frag_sum(fa[cur][ti], cs[ti]); \
+      }                                                                                           \
+      _Pragma("unroll") for (int ti = 0; ti < TI; ti++)                                           \
+        _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) mma16(acc[ti][tj], fb[cur][tj], fa[cur][ti]); \
     }                                                                                             \
-    _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) fb[tj] = OB::frag(BS, wj * WTJ + tj * 32, ks, lane); \
-    _Pragma("unroll") for (int ti = 0; ti < TI; ti++)                                             \
-      _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) mma16(acc[ti][tj], fb[tj], fa[ti]);       \
   }
-
-  // Bias gradient: sum_r A(i, r) from the A fragments already in registers,
-  // by the waves of the first column tile (wj == 0 of bj == 0); each lane adds
-  // its 8 reduction values per fragment in a fixed order.
-  const bool do_cs = AT == 1 && EPI == EPI_F32 && g.colsum != nullptr && bj == 0 && wj == 0;
-  float cs[TI];
-#pragma unroll
-  for (int ti = 0; ti < TI; ti++) cs[ti] = 0.f;
 
   // Two register stages: the tile two steps ahead is loaded while the current
   // one is consumed from LDS and the next one is stored to the other buffer.
-  OA a0, a1;
-  OB b0, b1;
-  a0.load(A, g.lda, i0, g.M, kbeg, tid);
-  b0.load(Bm, g.ldb, j0, g.N, kbeg, tid);
-  if (nk > 1) {
-    a1.load(A, g.lda, i0, g.M, kbeg + BK, tid);
-    b1.load(Bm, g.ldb, j0, g.N, kbeg + BK, tid);
-  }
-  a0.store(sA[0], tid);
-  b0.store(sB[0], tid);
-  __syncthreads();
-  for (int kt = 0; kt + 2 <= nk; kt += 2) {
-    // buffer 0 holds tile kt, registers 1 hold tile kt+1
-    if (kt + 2 < nk) {
-      a0.load(A, g.lda, i0, g.M, kbeg + (kt + 2) * BK, tid);
-      b0.load(Bm, g.ldb, j0, g.N, kbeg + (kt + 2) * BK, tid);
-    }
-    GEMM_COMPUTE(sA[0], sB[0])
-    a1.store(sA[1], tid);
-    b1.store(sB[1], tid);
-    __syncthreads();
-    // buffer 1 holds tile kt+1, registers 0 hold tile kt+2
-    if (kt + 3 < nk) {
-      a1.load(A, g.lda, i0, g.M, kbeg + (kt + 3) * BK, tid);
-      b1.load(Bm, g.ldb, j0, g.N, kbeg + (kt + 3) * BK, tid);
-    }
-    GEMM_COMPUTE(sA[1], sB[1])
-    if (kt + 2 < nk) {
-      a0.store(sA[0], tid);
-      b0.store(sB[0], tid);
-    }
-    __syncthreads();
-  }
-  if (nk & 1) {  // the last tile sits in buffer 0
-    GEMM_COMPUTE(sA[0], sB[0])
+  // Loads and stores are unconditional (tile indices past the end re-read the
+  // last tile, which is then never consumed): with no branch around them the
+  // compiler can leave the newest loads in flight at every LDS store instead
+  // of draining the whole load queue.
+#define GEMM_MAINLOOP(CSV)                                                                        \
+  {                                                                                               \
+    OA a0, a1;                                                                                    \
+    OB b0, b1;                                                                                    \
+    const int klast = kbeg + (nk - 1) * BK;                                                       \
+    a0.load(A, g.lda, i0, g.M, kbeg, tid);                                                        \
+    b0.load(Bm, g.ldb, j0, g.N, kbeg, tid);                                                       \
+    a1.load(A, g.lda, i0, g.M, min(kbeg + BK, klast), tid);                                       \
+    b1.load(Bm, g.ldb, j0, g.N, min(kbeg + BK, klast), tid);                                      \
+    a0.store(sA[0], tid);                                                                         \
+    b0.store(sB[0], tid);                                                                         \
+    __syncthreads();                                                                              \
+    for (int kt = 0; kt + 2 <= nk; kt += 2) {                                                     \
+      /* buffer 0 holds tile kt, registers 1 hold tile kt+1 */                                    \
+      const int k2 = min(kbeg + (kt + 2) * BK, klast), k3 = min(kbeg + (kt + 3) * BK, klast);     \
+      a0.load(A, g.lda, i0, g.M, k2, tid);                                                        \
+      b0.load(Bm, g.ldb, j0, g.N, k2, tid);                                                       \
+      GEMM_COMPUTE(sA[0], sB[0], CSV)                                                             \
+      a1.store(sA[1], tid);                                                                       \
+      b1.store(sB[1], tid);                                                                       \
+      __syncthreads();                                                                            \
+      /* buffer 1 holds tile kt+1, registers 0 hold tile kt+2 */                                  \
+      a1.load(A, g.lda, i0, g.M, k3, tid);                                                        \
+      b1.load(Bm, g.ldb, j0, g.N, k3, tid);                                                       \
+      GEMM_COMPUTE(sA[1], sB[1], CSV)                                                             \
+      a0.store(sA[0], tid);                                                                       \
+      b0.store(sB[0], tid);                                                                       \
+      __syncthreads();                                                                            \
+    }                                                                                             \
+    if (nk & 1) { /* the last tile sits in buffer 0 */                                            \
+      GEMM_COMPUTE(sA[0], sB[0], CSV)                                                             \
+    }                                                                                             \
   }
 
+  // Only the blocks of the first column tile (bj == 0) sum the bias gradient
+  // (and of those only the waves with wj == 0 write it).  The choice is made
+  // once per block, outside the main loop, so the loop itself stays one
+  // branch-free block and every wave passes the same barriers.
+  const bool do_cs = HAS_CS && g.colsum != nullptr && bj == 0;
+  float cs[TI];
+#pragma unroll
+  for (int ti = 0; ti < TI; ti++) cs[ti] = 0.f;
+  if constexpr (HAS_CS) {
+    if (do_cs) GEMM_MAINLOOP(1) else GEMM_MAINLOOP(0)
+  } else {
+    GEMM_MAINLOOP(0)
+  }
+
+#undef GEMM_MAINLOOP
 #undef GEMM_COMPUTE
-  if (do_cs) {
+#undef GEMM_FRAGS
+  if (do_cs && wj == 0) {
 #pragma unroll
     for (int ti = 0; ti < TI; ti++) {
       const float t = cs[ti] + __shfl_xor(cs[ti], 32, 64);  // the two halves of each row's reduction values
@@ -293,8 +327,9 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
   constexpr int BK = sizeof(T) == 2 ? 64 : 32;
   constexpr int VE = Vec16<T>::n;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  if (g.splits < 1 || g.K % (g.splits * BK) != 0 || g.M % VE != 0 || g.N % 8 != 0 || g.lda % VE != 0 ||
-      g.ldb % VE != 0 || (EPI != EPI_F32 && g.splits != 1))
+  if (g.K <= 0 || g.splits < 1 || g.K % (g.splits * BK) != 0 || g.M % VE != 0 || g.N % 8 != 0 || g.lda % VE != 0 ||
+      g.ldb % VE != 0 || (EPI != EPI_F32 && g.splits != 1) ||
+      (g.colsum != nullptr && !gemm_has_colsum(AT, EPI, WI * WJ)))
     return hipErrorInvalidValue;
   const int nbi = (g.M + BM - 1) / BM, nbj = (g.N + BN - 1) / BN;
   dim3 grid(nbi * nbj, g.splits);
@@ -302,17 +337,24 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
   return hipGetLastError();
 }
 
-// Tile shape per operand layout and output shape (bf16), from a sweep of the
-// step's matmuls on MI355X: 256x192 (4 waves) wherever the output width is a
-// multiple of 192, 256x256 with 8 waves for the large weight gradient (tied
-// output layer), 128x128 otherwise.  The weight-gradient split-K factor is
-// chosen so every configuration fills the 256 CUs.
+// Tile shape per operand layout and product shape (bf16), from a sweep of the
+// step's matmuls on MI355X.  The 128x128 tile runs two blocks per CU (two
+// waves per SIMD), which hides its prologue and epilogue behind the other
+// block's main loop; it wins wherever the reduction is short.  The 256x192
+// tile (one wave per SIMD, 1.5x the operand reuse) wins on long reductions and
+// on the smallest weight gradient; the 8-wave 256x256 tile serves the large
+// weight gradient of the tied output layer.
 enum TileKind { TILE_128 = 0, TILE_256x192 = 1, TILE_256_W8 = 2 };
 
-TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N) {
+TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
   if (p != BF16 || M < 256) return TILE_128;
-  if (a_t && b_t && (int64_t)M * N >= 8000000) return TILE_256_W8;
-  if (N % 192 == 0) return TILE_256x192;
+  const int64_t mn = (int64_t)M * N;
+  if (a_t && b_t) {
+    if (mn >= 8000000) return TILE_256_W8;
+    if (mn <= 1000000 && N % 192 == 0) return TILE_256x192;
+    return TILE_128;
+  }
+  if (K >= 2048 && N % 192 == 0) return TILE_256x192;
   return TILE_128;
 }
 
@@ -344,12 +386,13 @@ hipError_t dispatch(hipStream_t st, int a_t, int b_t, int epi, const GemmArgs& g
 }  // namespace
 
 hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArgs& g) {
-  const TileKind k = choose_tile(p, a_t, b_t, g.M, g.N);
+  TileKind k = choose_tile(p, a_t, b_t, g.M, g.N, g.K);
+  if (k == TILE_256_W8 && g.colsum) k = TILE_256x192;  // the 8-wave tile has no bias-gradient path
   return p == BF16 ? dispatch<bf16>(st, a_t, b_t, epi, g, k) : dispatch<float>(st, a_t, b_t, epi, g, k);
 }
 
 int gemm_split_hint(Prec p, int a_t, int b_t, int M, int N, int K) {
-  const TileKind k = choose_tile(p, a_t, b_t, M, N);
+  const TileKind k = choose_tile(p, a_t, b_t, M, N, K);
   const int bm = k == TILE_128 ? 128 : 256, bn = k == TILE_256x192 ? 192 : (k == TILE_256_W8 ? 256 : 128);
   const int bk = p == BF16 ? 64 : 32;
   const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
