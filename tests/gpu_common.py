@@ -49,7 +49,10 @@ def gpu_step(model, B, T, precision, params, micro_batches, step=1, lr=6e-4, cli
 
 
 def oracle_step(model, params, micro_batches, step=1, lr=6e-4, clip=1.0, wd=0.1, R=np.float64):
-    """The same step in the CPU oracle.  Grads are reported before clipping."""
+    """The same step in the CPU oracle.  Grads are reported before clipping.
+    R is the precision of forward and backward; the global norm, clipping and
+    AdamW always run in fp64 (an fp32 running sum of squares over ~1e8
+    gradients drops the small terms)."""
     K = len(micro_batches)
     p = params.astype(R).copy()
     g = np.zeros_like(p)
@@ -59,11 +62,13 @@ def oracle_step(model, params, micro_batches, step=1, lr=6e-4, clip=1.0, wd=0.1,
         rl = np.zeros(B * T, dtype=R)
         out["loss"].append(oracle.fwd_bwd(model, B, T, p, ids, tgt, 1.0 / K, g, rl, R=R))
         out["rows"].append(rl.astype(np.float64))
-    out["grads"] = g.astype(np.float64).copy()
+    g = g.astype(np.float64)
+    p = params.astype(np.float64).copy()
+    out["grads"] = g.copy()
     m = np.zeros_like(p)
     v = np.zeros_like(p)
-    out["norm"] = oracle.clip_grads(g, clip, R=R)
-    oracle.adamw(model, p, g, m, v, step, lr, 0.9, 0.95, 1e-8, wd, R=R)
+    out["norm"] = oracle.clip_grads(g, clip, R=np.float64)
+    oracle.adamw(model, p, g, m, v, step, lr, 0.9, 0.95, 1e-8, wd, R=np.float64)
     out["params"] = p.astype(np.float64)
     out["m"] = m.astype(np.float64)
     out["v"] = v.astype(np.float64)
@@ -75,3 +80,40 @@ def batches(model, B, T, K, seed, data="zipf", index0=0):
     stream = synth.zipf_stream(n, model.vocab_size, seed) if data == "zipf" else synth.uniform_stream(
         n, model.vocab_size, seed)
     return [synth.micro_batch(stream, B, T, index0 + k) for k in range(K)]
+
+
+# Parity bar: fp32 mode |loss diff| <= 1e-4 and per-tensor gradient relative
+# L2 <= 1e-4; bf16 mode |loss diff| <= 2e-2, parameter and per-tensor gradient
+# relative L2 <= 3e-2 after one step.  Per-position losses: 1e-4 / 1e-1.
+TOL = {"fp32": dict(loss=1e-4, grad=1e-4, param=1e-4, rows=1e-4),
+       "bf16": dict(loss=2e-2, grad=3e-2, param=3e-2, rows=1e-1)}
+
+
+def compare(model, g, o, prec, check_rows=True):
+    tol = TOL[prec]
+    print(f"loss gpu {g['loss']} oracle {o['loss']}  norm gpu {g['norm']:.6f} oracle {o['norm']:.6f}", flush=True)
+    assert g["status"] == 0
+    for a, b in zip(g["loss"], o["loss"]):
+        assert abs(a - b) <= tol["loss"], (a, b)
+    if check_rows:
+        for a, b in zip(g["rows"], o["rows"]):
+            assert np.max(np.abs(a - b)) <= tol["rows"], np.max(np.abs(a - b))
+    lay = binding.param_layout(model)
+    gv, ov = tensor_views(lay, g["grads"]), tensor_views(lay, o["grads"])
+    worst = max((rel_l2(gv[n], ov[n]), n) for n in gv if np.linalg.norm(ov[n]) > 0)
+    print(f"worst per-tensor grad rel L2: {worst[0]:.2e} ({worst[1]})", flush=True)
+    for n in gv:
+        if np.linalg.norm(ov[n]) == 0:
+            assert np.all(gv[n] == 0), n
+        else:
+            assert rel_l2(gv[n], ov[n]) <= tol["grad"], (n, rel_l2(gv[n], ov[n]))
+    # exact: rows of wte that receive any gradient (tokens seen + every real row via the head)
+    wte_g = gv["wte"].reshape(model.padded_vocab_size, -1)
+    assert np.all(wte_g[model.vocab_size:] == 0)
+    assert abs(g["norm"] - o["norm"]) <= tol["grad"] * o["norm"]
+    assert rel_l2(g["params"], o["params"]) <= tol["param"]
+    mv, ovm = tensor_views(lay, g["m"]), tensor_views(lay, o["m"])
+    for n in mv:
+        if np.linalg.norm(ovm[n]) > 0:
+            assert rel_l2(mv[n], ovm[n]) <= tol["grad"], n
+    return worst

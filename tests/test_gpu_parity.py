@@ -13,48 +13,15 @@ import math
 import numpy as np
 import pytest
 
-from gpu_common import batches, gpu_step, oracle_step, rel_l2, tensor_views
+from gpu_common import batches, compare, gpu_step, oracle_step
 from transformer_lm_pretraining_gpt2_amd import binding, synth
 from transformer_lm_pretraining_gpt2_amd.config import CONFIGS, GPT2Config
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"fp32": dict(loss=1e-4, grad=1e-4, param=1e-4, rows=1e-4),
-       "bf16": dict(loss=2e-2, grad=3e-2, param=3e-2, rows=1e-1)}
-
 TINY = CONFIGS["tiny"].model
 PADDED = GPT2Config(vocab_size=509, padded_vocab_size=512, n_layer=2, n_head=4, n_embd=128, max_seq_len=128)
 SMALL = CONFIGS["small"].model
-
-
-def compare(model, g, o, prec, check_rows=True):
-    tol = TOL[prec]
-    print(f"loss gpu {g['loss']} oracle {o['loss']}  norm gpu {g['norm']:.6f} oracle {o['norm']:.6f}", flush=True)
-    assert g["status"] == 0
-    for a, b in zip(g["loss"], o["loss"]):
-        assert abs(a - b) <= tol["loss"], (a, b)
-    if check_rows:
-        for a, b in zip(g["rows"], o["rows"]):
-            assert np.max(np.abs(a - b)) <= tol["rows"], np.max(np.abs(a - b))
-    lay = binding.param_layout(model)
-    gv, ov = tensor_views(lay, g["grads"]), tensor_views(lay, o["grads"])
-    worst = max((rel_l2(gv[n], ov[n]), n) for n in gv if np.linalg.norm(ov[n]) > 0)
-    print(f"worst per-tensor grad rel L2: {worst[0]:.2e} ({worst[1]})", flush=True)
-    for n in gv:
-        if np.linalg.norm(ov[n]) == 0:
-            assert np.all(gv[n] == 0), n
-        else:
-            assert rel_l2(gv[n], ov[n]) <= tol["grad"], (n, rel_l2(gv[n], ov[n]))
-    # exact: rows of wte that receive any gradient (tokens seen + every real row via the head)
-    wte_g = gv["wte"].reshape(model.padded_vocab_size, -1)
-    assert np.all(wte_g[model.vocab_size:] == 0)
-    assert abs(g["norm"] - o["norm"]) <= tol["grad"] * o["norm"]
-    assert rel_l2(g["params"], o["params"]) <= tol["param"]
-    mv, ovm = tensor_views(lay, g["m"]), tensor_views(lay, o["m"])
-    for n in mv:
-        if np.linalg.norm(ovm[n]) > 0:
-            assert rel_l2(mv[n], ovm[n]) <= tol["grad"], n
-    return worst
 
 
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])

@@ -42,8 +42,17 @@ struct Operand {
   static_assert((R * BK / VE) % NT == 0, "tile does not split evenly over threads");
   typedef typename Frag<T>::type F;
   f32x4 reg[PER];
+  // Global loads go through a buffer descriptor (base address in scalar
+  // registers): each chunk keeps one loop-invariant 32-bit byte offset and the
+  // reduction step is a uniform scalar offset.  The host checks that every
+  // operand spans less than 4 GiB.
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff[PER];
+  int64_t kstride;  // bytes per reduction index
 
-  __device__ __forceinline__ void load(const T* X, int64_t ld, int row0, int nrows, int k0, int tid) {
+  __device__ __forceinline__ void init(const T* X, int64_t ld, int row0, int nrows, int tid) {
+    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(X), 0, -1, 0x00020000);
+    kstride = TRANS ? ld * (int64_t)sizeof(T) : (int64_t)sizeof(T);
 #pragma unroll
     for (int c = 0; c < PER; c++) {
       const int idx = tid + c * NT;
@@ -51,12 +60,18 @@ struct Operand {
       if constexpr (TRANS == 0) {
         // rows past the edge re-read the last row: they only feed outputs the epilogue drops
         const int r = min(row0 + gr, nrows - 1);
-        reg[c] = *reinterpret_cast<const f32x4*>(X + (int64_t)r * ld + k0 + gc * VE);
+        voff[c] = (uint32_t)(((int64_t)r * ld + gc * VE) * (int64_t)sizeof(T));
       } else {
         const int col = min(row0 + gc * VE, nrows - VE);
-        reg[c] = *reinterpret_cast<const f32x4*>(X + (int64_t)(k0 + gr) * ld + col);
+        voff[c] = (uint32_t)(((int64_t)gr * ld + col) * (int64_t)sizeof(T));
       }
     }
+  }
+  __device__ __forceinline__ void load(int k0) {
+    const int soff = (int)(k0 * kstride);
+#pragma unroll
+    for (int c = 0; c < PER; c++)
+      reg[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[c], soff, 0));
   }
   __device__ __forceinline__ void store(T* s, int tid) const {
 #pragma unroll
@@ -172,13 +187,13 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
 #define GEMM_FRAGS(AS, BS, KS, FA, FB)                                                            \
   _Pragma("unroll") for (int ti = 0; ti < TI; ti++) FA[ti] = OA::frag(AS, wi * WTI + ti * 32, KS, lane); \
   _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) FB[tj] = OB::frag(BS, wj * WTJ + tj * 32, KS, lane);
-#define GEMM_COMPUTE(AS, BS, CSV)                                                                 \
+#define GEMM_COMPUTE(AS, BS, CSV, PP)                                                             \
   {                                                                                               \
     F fa[2][TI], fb[2][TJ];                                                                       \
-    if constexpr (PIPE) { GEMM_FRAGS(AS, BS, 0, fa[0], fb[0]) }                                   \
+    if constexpr (PP) { GEMM_FRAGS(AS, BS, 0, fa[0], fb[0]) }                                     \
     _Pragma("unroll") for (int ks = 0; ks < BK / 16; ks++) {                                      \
-      const int cur = PIPE ? ks & 1 : 0;                                                          \
-      if constexpr (PIPE) {                                                                       \
+      const int cur = PP ? ks & 1 : 0;                                                            \
+      if constexpr (PP) {                                                                         \
         if (ks + 1 < BK / 16) { GEMM_FRAGS(AS, BS, ks + 1, fa[cur ^ 1], fb[cur ^ 1]) }            \
       } else {                                                                                    \
         GEMM_FRAGS(AS, BS, ks, fa[0], fb[0])                                                      \
@@ -201,33 +216,37 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   {                                                                                               \
     OA a0, a1;                                                                                    \
     OB b0, b1;                                                                                    \
+    a0.init(A, g.lda, i0, g.M, tid);                                                              \
+    b0.init(Bm, g.ldb, j0, g.N, tid);                                                             \
+    a1.init(A, g.lda, i0, g.M, tid);                                                              \
+    b1.init(Bm, g.ldb, j0, g.N, tid);                                                             \
     const int klast = kbeg + (nk - 1) * BK;                                                       \
-    a0.load(A, g.lda, i0, g.M, kbeg, tid);                                                        \
-    b0.load(Bm, g.ldb, j0, g.N, kbeg, tid);                                                       \
-    a1.load(A, g.lda, i0, g.M, min(kbeg + BK, klast), tid);                                       \
-    b1.load(Bm, g.ldb, j0, g.N, min(kbeg + BK, klast), tid);                                      \
+    a0.load(kbeg);                                                                                \
+    b0.load(kbeg);                                                                                \
+    a1.load(min(kbeg + BK, klast));                                                               \
+    b1.load(min(kbeg + BK, klast));                                                               \
     a0.store(sA[0], tid);                                                                         \
     b0.store(sB[0], tid);                                                                         \
     __syncthreads();                                                                              \
     for (int kt = 0; kt + 2 <= nk; kt += 2) {                                                     \
       /* buffer 0 holds tile kt, registers 1 hold tile kt+1 */                                    \
       const int k2 = min(kbeg + (kt + 2) * BK, klast), k3 = min(kbeg + (kt + 3) * BK, klast);     \
-      a0.load(A, g.lda, i0, g.M, k2, tid);                                                        \
-      b0.load(Bm, g.ldb, j0, g.N, k2, tid);                                                       \
-      GEMM_COMPUTE(sA[0], sB[0], CSV)                                                             \
+      a0.load(k2);                                                                                \
+      b0.load(k2);                                                                                \
+      GEMM_COMPUTE(sA[0], sB[0], CSV, PIPE)                                                       \
       a1.store(sA[1], tid);                                                                       \
       b1.store(sB[1], tid);                                                                       \
       __syncthreads();                                                                            \
       /* buffer 1 holds tile kt+1, registers 0 hold tile kt+2 */                                  \
-      a1.load(A, g.lda, i0, g.M, k3, tid);                                                        \
-      b1.load(Bm, g.ldb, j0, g.N, k3, tid);                                                       \
-      GEMM_COMPUTE(sA[1], sB[1], CSV)                                                             \
+      a1.load(k3);                                                                                \
+      b1.load(k3);                                                                                \
+      GEMM_COMPUTE(sA[1], sB[1], CSV, PIPE)                                                       \
       a0.store(sA[0], tid);                                                                       \
       b0.store(sB[0], tid);                                                                       \
       __syncthreads();                                                                            \
     }                                                                                             \
-    if (nk & 1) { /* the last tile sits in buffer 0 */                                            \
-      GEMM_COMPUTE(sA[0], sB[0], CSV)                                                             \
+    if (nk & 1) { /* the last tile sits in buffer 0 (no read-ahead: registers are tight here) */  \
+      GEMM_COMPUTE(sA[0], sB[0], CSV, false)                                                      \
     }                                                                                             \
   }
 
@@ -339,11 +358,11 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
 
 // Tile shape per operand layout and product shape (bf16), from a sweep of the
 // step's matmuls on MI355X.  The 128x128 tile runs two blocks per CU (two
-// waves per SIMD), which hides its prologue and epilogue behind the other
-// block's main loop; it wins wherever the reduction is short.  The 256x192
-// tile (one wave per SIMD, 1.5x the operand reuse) wins on long reductions and
-// on the smallest weight gradient; the 8-wave 256x256 tile serves the large
-// weight gradient of the tied output layer.
+// waves per SIMD), which hides one block's prologue and epilogue behind the
+// other's main loop; it wins wherever the product is small.  The 8-wave
+// 256x256 tile (also two waves per SIMD, twice the operand reuse) wins on long
+// reductions and large outputs, and on the tied output layer's weight
+// gradient; the 4-wave 256x192 tile only on the smallest weight gradient.
 enum TileKind { TILE_128 = 0, TILE_256x192 = 1, TILE_256_W8 = 2 };
 
 TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
@@ -354,16 +373,16 @@ TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
     if (mn <= 1000000 && N % 192 == 0) return TILE_256x192;
     return TILE_128;
   }
-  if (K >= 2048 && N % 192 == 0) return TILE_256x192;
+  if (K >= 2048 || mn >= 40000000) return TILE_256_W8;
   return TILE_128;
 }
 
 template <typename T, int AT, int BT, int EPI>
 hipError_t launch_tiled(hipStream_t st, const GemmArgs& g, TileKind k) {
   if constexpr (sizeof(T) == 2) {
-    if (k == TILE_256x192) return launch<T, 256, 192, 2, 2, AT, BT, EPI>(st, g);
-    if constexpr (AT && BT)
-      if (k == TILE_256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI>(st, g);
+    if (k == TILE_256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI>(st, g);
+    if constexpr (AT == 1)
+      if (k == TILE_256x192) return launch<T, 256, 192, 2, 2, AT, BT, EPI>(st, g);
   }
   return launch<T, 128, 128, 2, 2, AT, BT, EPI>(st, g);
 }
