@@ -347,7 +347,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
 // reads), and the tile's LSE and D values.
 // ------------------------------------------------------------------------
 template <typename T, int HD>
-__global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
+__global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
                                                            const float* __restrict__ lse, const float* __restrict__ dsum,
                                                            T* __restrict__ dqkv, int T_, int NH, float sl2,
                                                            float scale) {
@@ -418,33 +418,43 @@ __global__ void __launch_bounds__(NW * 64) attn_dkv_kernel(const T* __restrict__
     }
     if (active && qt0 + KT - 1 >= k0) {
       const bool diag = qt0 < k0 + WQ - 1;
-      f32x16 s[2], dp[2];
+      // the tile's two 32-query halves one after the other: only one S and
+      // one dP accumulator are live at a time
 #pragma unroll
       for (int c2 = 0; c2 < 2; c2++) {
-        s[c2] = f32x16{};
-        dp[c2] = f32x16{};
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ds = 0; ds < ND; ds++) {
-          mma16(s[c2], ld8(Qs[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), kf[ds]);
-          mma16(dp[c2], ld8(Ds[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), vf[ds]);
+          mma16(s, ld8(Qs[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), kf[ds]);
+          mma16(dp, ld8(Ds[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), vf[ds]);
         }
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int ql = c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          float p = fast_exp2(fmaf(s[c2][r], sl2, -Ls[cur][ql]));
-          if (diag && qt0 + ql < kv) p = 0.f;
-          s[c2][r] = p;
-          dp[c2][r] = p * (dp[c2][r] - Dd[cur][ql]);
+          s[r] = fast_exp2(fmaf(s[r], sl2, -Ls[cur][ql]));
         }
-      }
+        if (diag) {  // causal mask: only tiles that straddle this wave's keys
 #pragma unroll
-      for (int c = 0; c < KT / 16; c++) {
-        const F pf = acc_frag<T>(s[c / 2], c % 2);
-        const F sf = acc_frag<T>(dp[c / 2], c % 2);
+          for (int r = 0; r < 16; r++) {
+            const int ql = c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+            if (qt0 + ql < kv) s[r] = 0.f;
+          }
+        }
 #pragma unroll
-        for (int dt = 0; dt < NDT; dt++) {
-          mma16(dv[dt], ld_tsplit<T, LD>(Ds[cur], dt * 32, c, lane), pf);
-          mma16(dk[dt], ld_tsplit<T, LD>(Qs[cur], dt * 32, c, lane), sf);
+        for (int r = 0; r < 16; r++) {
+          const int ql = c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
+          dp[r] = s[r] * (dp[r] - Dd[cur][ql]);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; h2++) {
+          const int c = 2 * c2 + h2;
+          const F pf = acc_frag<T>(s, h2);
+          const F sf = acc_frag<T>(dp, h2);
+#pragma unroll
+          for (int dt = 0; dt < NDT; dt++) {
+            mma16(dv[dt], ld_tsplit<T, LD>(Ds[cur], dt * 32, c, lane), pf);
+            mma16(dk[dt], ld_tsplit<T, LD>(Qs[cur], dt * 32, c, lane), sf);
+          }
         }
       }
     }
