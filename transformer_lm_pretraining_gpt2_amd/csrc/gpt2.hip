@@ -105,7 +105,12 @@ struct Plan {
   std::vector<int64_t> x_in, x_mid, h1, h2, mean1, rstd1, mean2, rstd2, qkv, atty, lse, u, g;
   int64_t hf, meanf, rstdf, logits, loss_rows, loss_tmp;
   int64_t dres, dres_lp, dh, datty, dqkv, du, dsum, piece;
-  int64_t wpart, lnpart, cspart, normpart;
+  // reduction partials, one buffer per producer so a whole layer's partial
+  // sums can be reduced by one launch: weight kinds (qkv, proj, fc, fcproj)
+  // for the split-K products and their bias column sums; LayerNorm slots
+  // (final, ln_2, ln_1) for the gain/bias partials
+  int64_t wpart[4], cspart[4], lnpart[3];
+  int64_t normpart;
   int64_t ska, sva, skb, svb, seg, nseg;
   int64_t flags, scale, norm;
   std::vector<int> split;  // split-K factor per layer weight kind (qkv, proj, fc, fcproj)
@@ -154,12 +159,12 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
   const int Mi = (int)M, Ci = (int)C;
   P.split = {gemm_split_hint(pr, 1, 1, 3 * Ci, Ci, Mi), gemm_split_hint(pr, 1, 1, Ci, Ci, Mi),
              gemm_split_hint(pr, 1, 1, 4 * Ci, Ci, Mi), gemm_split_hint(pr, 1, 1, Ci, 4 * Ci, Mi)};
-  int64_t wmax = 0;
-  const int64_t wsz[4] = {3 * C * C, C * C, 4 * C * C, 4 * C * C};
-  for (int k = 0; k < 4; k++) wmax = std::max(wmax, (int64_t)P.split[k] * wsz[k]);
-  P.wpart = take(4 * wmax);
-  P.lnpart = take(4 * (int64_t)layernorm_bwd_parts((int)M) * 2 * C);
-  P.cspart = take(4 * (int64_t)16 * 4 * C);  // bias-gradient partials: splits (<= 16) x out width
+  const int64_t wsz[4] = {3 * C * C, C * C, 4 * C * C, 4 * C * C}, wout[4] = {3 * C, C, 4 * C, C};
+  for (int k = 0; k < 4; k++) {
+    P.wpart[k] = P.split[k] > 1 ? take(4 * (int64_t)P.split[k] * wsz[k]) : 0;
+    P.cspart[k] = take(4 * (int64_t)P.split[k] * wout[k]);
+  }
+  for (int k = 0; k < 3; k++) P.lnpart[k] = take(4 * (int64_t)layernorm_bwd_parts((int)M) * 2 * C);
   P.normpart = take(8 * (int64_t)grad_norm_parts());
   P.ska = take(4 * M);
   P.sva = take(4 * M);
@@ -196,6 +201,7 @@ struct gpt2_handle {
   Plan plan;
   std::vector<const Tensor*> by_kind_layer;  // [kind * (L+1) + layer+1]
   bool have_fwd = false, fwd_has_targets = false;
+  std::vector<ReduceJob> pending;  // partial sums not yet reduced (backward only)
   std::string err;
   int timed = -1;
   std::vector<TimedLaunch> timings;
@@ -313,11 +319,35 @@ GemmArgs dx_args(gpt2_t* h, const void* dY, const void* W, int N, int K, void* o
   return g;
 }
 
+// Partial sums wait in a queue until the layer's backward is done; then one
+// launch reduces them all (each into its own gradient, in a fixed order).
+void queue_reduction(gpt2_t* h, const float* part, int nparts, int64_t ld, float* out, int n, int accumulate) {
+  ReduceJob j;
+  j.part = part;
+  j.ld = ld;
+  j.out = out;
+  j.n = n;
+  j.nparts = nparts;
+  j.accumulate = accumulate;
+  h->pending.push_back(j);
+}
+
+int flush_reductions(gpt2_t* h) {
+  int rc = GPT2_OK;
+  for (size_t k = 0; k < h->pending.size() && !rc; k += kMaxReduceJobs) {
+    const int n = (int)std::min<size_t>(kMaxReduceJobs, h->pending.size() - k);
+    rc = hip_check(h, reduce_jobs(h->st, h->pending.data() + k, n), "reduce partials");
+  }
+  h->pending.clear();
+  return rc;
+}
+
 // Weight gradient of W [N, K]: dW (+)= dY^T X, dY [M, N], X [M, K], and the
 // bias gradient db (+)= sum_rows dY (column sums fused into the same product);
 // split-K partials are reduced in order into the gradient buffers.
-int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* dW, float* db, int splits,
+int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* dW, float* db, int wkind,
                 int accumulate, const char* what) {
+  const int splits = h->plan.split[wkind];
   GemmArgs g;
   g.A = dY;
   g.lda = N;
@@ -327,7 +357,7 @@ int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* d
   g.N = K;
   g.K = (int)h->M;
   g.splits = splits;
-  float* cpart = h->w<float>(h->plan.cspart);
+  float* cpart = h->w<float>(h->plan.cspart[wkind]);
   if (db) {
     g.colsum = cpart;
     g.colsum_stride = N;
@@ -339,21 +369,21 @@ int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* d
     g.accumulate = accumulate;
     rc = run_gemm(h, K_GEMM_TN_F32, 1, 1, EPI_F32, g, what);
   } else {
-    float* part = h->w<float>(h->plan.wpart);
+    float* part = h->w<float>(h->plan.wpart[wkind]);
     g.C = part;
     g.ldc = K;
     g.split_stride = (int64_t)N * K;
     rc = run_gemm(h, K_GEMM_TN_F32, 1, 1, EPI_F32, g, what);
-    if (!rc) rc = hip_check(h, reduce_parts(h->st, part, splits, (int64_t)N * K, dW, N * K, accumulate), "reduce dW");
+    if (!rc) queue_reduction(h, part, splits, (int64_t)N * K, dW, N * K, accumulate);
   }
-  if (!rc && db) rc = hip_check(h, reduce_parts(h->st, cpart, splits, N, db, N, accumulate), "reduce db");
+  if (!rc && db) queue_reduction(h, cpart, splits, N, db, N, accumulate);
   return rc;
 }
 
 int ln_backward(gpt2_t* h, const void* dy, const float* x, const float* mean, const float* rstd, int kind_g, int layer,
-                int accumulate_dres, int accumulate_grads) {
+                int slot, int accumulate_dres, int accumulate_grads) {
   const int C = h->cfg.n_embd, M = (int)h->M;
-  float* part = h->w<float>(h->plan.lnpart);
+  float* part = h->w<float>(h->plan.lnpart[slot]);
   int nparts = 0;
   void* dres_lp = h->prec == BF16 ? h->w<void>(h->plan.dres_lp) : nullptr;
   Timer t(h, K_LN_BWD, 0);
@@ -363,8 +393,8 @@ int ln_backward(gpt2_t* h, const void* dy, const float* x, const float* mean, co
   int rc = hip_check(h, e, "layernorm_bwd");
   if (rc) return rc;
   // gain and bias gradients are adjacent in the layout: one reduction covers both
-  return hip_check(h, reduce_parts(h->st, part, nparts, 2 * C, h->G32(kind_g, layer), 2 * C, accumulate_grads),
-                   "reduce ln");
+  queue_reduction(h, part, nparts, 2 * C, h->G32(kind_g, layer), 2 * C, accumulate_grads);
+  return GPT2_OK;
 }
 
 }  // namespace
@@ -569,6 +599,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
   const gpt2_config_t& c = h->cfg;
   const int C = c.n_embd, L = c.n_layer, NH = c.n_head, hd = C / NH, Vp = c.padded_vocab_size;
   const Plan& P = h->plan;
+  h->pending.clear();
   const int acc = micro_step > 0;
   const float alpha = 1.0f / (float)grad_accum_steps;
   const bool lp = h->prec == BF16;
@@ -596,12 +627,12 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     if ((rc = run_gemm(h, K_GEMM_TN_LMHEAD, 1, 1, EPI_F32, w, "lm_head dw"))) return rc;
   }
   if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[L]), h->w<float>(P.meanf), h->w<float>(P.rstdf), T_LNFG,
-                        -1, 0, acc)))
+                        -1, 0, 0, acc)))
     return rc;
 
   for (int l = L - 1; l >= 0; l--) {
     // MLP down-projection: dres is the gradient of the block output
-    if ((rc = weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), P.split[3],
+    if ((rc = weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), 3,
                           acc, "fcproj dw")))
       return rc;
     g = dx_args(h, dres_op, h->W(T_FCPW, l), C, 4 * C, h->w<void>(P.du));
@@ -610,15 +641,15 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     if ((rc = run_gemm(h, K_GEMM_NN_GELU_BWD, 0, 1, EPI_GELU_BWD, g, "fcproj dx"))) return rc;
     // MLP up-projection
     if ((rc = weight_grad(h, h->w<void>(P.du), h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), h->G32(T_FCB, l),
-                          P.split[2], acc, "fc dw")))
+                          2, acc, "fc dw")))
       return rc;
     g = dx_args(h, h->w<void>(P.du), h->W(T_FCW, l), 4 * C, C, h->w<void>(P.dh));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "fc dx"))) return rc;
     if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_mid[l]), h->w<float>(P.mean2[l]), h->w<float>(P.rstd2[l]),
-                          T_LN2G, l, 1, acc)))
+                          T_LN2G, l, 1, 1, acc)))
       return rc;
     // attention output projection
-    if ((rc = weight_grad(h, dres_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l), P.split[1],
+    if ((rc = weight_grad(h, dres_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l), 1,
                           acc, "proj dw")))
       return rc;
     g = dx_args(h, dres_op, h->W(T_PROJW, l), C, C, h->w<void>(P.datty));
@@ -647,14 +678,16 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     }
     // qkv projection
     if ((rc = weight_grad(h, h->w<void>(P.dqkv), h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l), h->G32(T_QKVB, l),
-                          P.split[0], acc, "qkv dw")))
+                          0, acc, "qkv dw")))
       return rc;
     g = dx_args(h, h->w<void>(P.dqkv), h->W(T_QKVW, l), 3 * C, C, h->w<void>(P.dh));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "qkv dx"))) return rc;
     if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[l]), h->w<float>(P.mean1[l]), h->w<float>(P.rstd1[l]),
-                          T_LN1G, l, 1, acc)))
+                          T_LN1G, l, 2, 1, acc)))
       return rc;
+    if ((rc = flush_reductions(h))) return rc;
   }
+  if ((rc = flush_reductions(h))) return rc;
   // embeddings: position rows and the (tied) token rows, in a fixed order
   rc = hip_check(h, embed_bwd(h->st, dres, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva), h->w<int32_t>(P.seg),
                               h->w<int32_t>(P.nseg), h->G32(T_WTE), h->G32(T_WPE), h->w<float>(P.piece), h->B, h->T,

@@ -65,11 +65,23 @@ hipError_t layernorm_bwd(hipStream_t st, Prec p, const void* dy, const float* x,
                          int* nparts);
 int layernorm_bwd_parts(int M);
 
-// out[j] = (accumulate ? out[j] : 0) + sum_p part[p*ld + j]  (fixed order over p)
-hipError_t reduce_parts(hipStream_t st, const float* part, int nparts, int64_t ld, float* out, int n, int accumulate);
+// out[j] = [out[j] +] sum_{p < nparts} part[p*ld + j] for j < n (n, ld multiples
+// of 4), partials added in order; up to kMaxReduceJobs independent jobs per launch.
+constexpr int kMaxReduceJobs = 16;
+struct ReduceJob {
+  const float* part = nullptr;
+  int64_t ld = 0;
+  float* out = nullptr;
+  int n = 0, nparts = 0, accumulate = 0;
+  int block0 = 0;  // filled in by reduce_jobs
+};
+struct ReduceJobs {
+  ReduceJob j[kMaxReduceJobs];
+  int count;
+};
+hipError_t reduce_jobs(hipStream_t st, const ReduceJob* jobs, int count);
 
 // per-chunk column sums of X [M, N] (act type or fp32) into part [nchunks][N]
-hipError_t colsum_parts(hipStream_t st, Prec p, int x_is_f32, const void* X, int M, int N, float* part, int nchunks);
 
 // ---- embeddings ----
 hipError_t embed_fwd(hipStream_t st, const int32_t* idx, const int32_t* tgt, const float* wte, const float* wpe,

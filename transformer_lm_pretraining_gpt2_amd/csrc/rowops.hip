@@ -173,42 +173,59 @@ __global__ void __launch_bounds__(256) ln_bwd_kernel(const T* __restrict__ dy, c
     part[(int64_t)blockIdx.x * 2 * C + j] = ((sh[0][j] + sh[1][j]) + sh[2][j]) + sh[3][j];
 }
 
-// out[j] = [out[j] +] sum_p part[p*ld + j].  A block of 16 waves covers 256
-// consecutive j (four per lane); wave w sums its contiguous range of p in
-// order, then the 16 wave sums are added in wave order.
-constexpr int RED_W = 16;
+// Batched partial-sum reduction: for every job, out[j] = [out[j] +]
+// sum_p part[p*ld + j], p in order.  One launch serves up to
+// kMaxReduceJobs jobs (all split-K, bias and LayerNorm partials of a layer).
+// A job with at most RED_SLICES partials gives each thread one 4-float output
+// chunk and adds its partials in order; a job with more splits the partials
+// into RED_SLICES contiguous ranges (summed in order by separate threads) and
+// adds the range sums in range order.  Either way the summation order is
+// fixed, so results are deterministic.
+constexpr int RED_SLICES = 16;
+constexpr int RED_THREADS = 256;
 
-__global__ void __launch_bounds__(RED_W * 64) reduce_parts_kernel(const float* __restrict__ part, int nparts,
-                                                                  int64_t ld, float* __restrict__ out, int n,
-                                                                  int accumulate) {
-  __shared__ f32x4 sh[RED_W][64];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t j = ((int64_t)blockIdx.x * 64 + lane) * 4;
-  const int p0 = (int)((int64_t)nparts * w / RED_W), p1 = (int)((int64_t)nparts * (w + 1) / RED_W);
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  if (j < n)
-    for (int p = p0; p < p1; p++) s += *reinterpret_cast<const f32x4*>(part + (int64_t)p * ld + j);
-  sh[w][lane] = s;
-  __syncthreads();
-  if (w == 0 && j < n) {
-    f32x4 t = sh[0][lane];
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+__global__ void __launch_bounds__(RED_THREADS) reduce_jobs_kernel(ReduceJobs jobs) {
+  __shared__ f32x4 sh[RED_THREADS];
+  int jb = 0;
+  while (jb + 1 < jobs.count && (int)blockIdx.x >= jobs.j[jb + 1].block0) jb++;
+  const ReduceJob& J = jobs.j[jb];
+  const int blk = blockIdx.x - J.block0, tid = threadIdx.x;
+  if (J.nparts <= RED_SLICES) {
+    const int64_t j = ((int64_t)blk * RED_THREADS + tid) * 4;
+    if (j >= J.n) return;
+    const float* src = J.part + j;
+    f32x4 v[RED_SLICES];
 #pragma unroll
-    for (int k = 1; k < RED_W; k++) t += sh[k][lane];
-    if (accumulate) t += *reinterpret_cast<const f32x4*>(out + j);
-    *reinterpret_cast<f32x4*>(out + j) = t;
+    for (int p = 0; p < RED_SLICES; p++)
+      if (p < J.nparts) v[p] = ld4(src + p * J.ld);
+    f32x4 t = v[0];
+#pragma unroll
+    for (int p = 1; p < RED_SLICES; p++)
+      if (p < J.nparts) t += v[p];
+    if (J.accumulate) t += ld4(J.out + j);
+    *reinterpret_cast<f32x4*>(J.out + j) = t;
+  } else {
+    constexpr int CH = RED_THREADS / RED_SLICES;  // output chunks per block
+    const int slice = tid / CH, c = tid % CH;
+    const int64_t j = ((int64_t)blk * CH + c) * 4;
+    const int p0 = (int)((int64_t)J.nparts * slice / RED_SLICES), p1 = (int)((int64_t)J.nparts * (slice + 1) / RED_SLICES);
+    f32x4 t = {0.f, 0.f, 0.f, 0.f};
+    if (j < J.n)
+      for (int p = p0; p < p1; p++) t += ld4(J.part + (int64_t)p * J.ld + j);
+    sh[tid] = t;
+    __syncthreads();
+    if (slice == 0 && j < J.n) {
+      f32x4 u = sh[c];
+#pragma unroll
+      for (int k = 1; k < RED_SLICES; k++) u += sh[k * CH + c];
+      if (J.accumulate) u += ld4(J.out + j);
+      *reinterpret_cast<f32x4*>(J.out + j) = u;
+    }
   }
 }
 
-// part[chunk][j] = sum over rows of the chunk of X[row][j] (rows in order)
-template <typename T>
-__global__ void colsum_kernel(const T* __restrict__ X, int M, int N, float* __restrict__ part, int rows_per_chunk) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= N) return;
-  const int r0 = blockIdx.y * rows_per_chunk, r1 = min(M, r0 + rows_per_chunk);
-  float s = 0.f;
-  for (int r = r0; r < r1; r++) s += to_f<T>(X[(int64_t)r * N + j]);
-  part[(int64_t)blockIdx.y * N + j] = s;
-}
 
 // ---------------------------------------------------------------------------
 // Embedding forward: x[b,t] = wte[id[b,t]] + wpe[t]  (one wave per row).
@@ -639,20 +656,22 @@ hipError_t layernorm_bwd(hipStream_t st, Prec p, const void* dy, const float* x,
   return hipGetLastError();
 }
 
-hipError_t reduce_parts(hipStream_t st, const float* part, int nparts, int64_t ld, float* out, int n, int accumulate) {
-  if (n % 4 != 0 || ld % 4 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3((n / 4 + 63) / 64), dim3(RED_W * 64), 0, st, part, nparts, ld, out, n,
-                     accumulate);
-  return hipGetLastError();
-}
-
-hipError_t colsum_parts(hipStream_t st, Prec p, int x_is_f32, const void* X, int M, int N, float* part, int nchunks) {
-  const int rpc = (M + nchunks - 1) / nchunks;
-  dim3 grid((N + 255) / 256, nchunks);
-  if (x_is_f32 || p == F32)
-    hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(256), 0, st, static_cast<const float*>(X), M, N, part, rpc);
-  else
-    hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(256), 0, st, static_cast<const bf16*>(X), M, N, part, rpc);
+hipError_t reduce_jobs(hipStream_t st, const ReduceJob* jobs, int count) {
+  if (count <= 0) return hipSuccess;
+  if (count > kMaxReduceJobs) return hipErrorInvalidValue;
+  ReduceJobs J;
+  J.count = count;
+  int blocks = 0;
+  for (int k = 0; k < count; k++) {
+    J.j[k] = jobs[k];
+    const ReduceJob& q = jobs[k];
+    if (q.n % 4 != 0 || q.ld % 4 != 0 || q.nparts < 1 || q.part == nullptr || q.out == nullptr)
+      return hipErrorInvalidValue;
+    J.j[k].block0 = blocks;
+    const int per = q.nparts <= RED_SLICES ? RED_THREADS * 4 : (RED_THREADS / RED_SLICES) * 4;
+    blocks += (q.n + per - 1) / per;
+  }
+  hipLaunchKernelGGL(reduce_jobs_kernel, dim3(blocks), dim3(RED_THREADS), 0, st, J);
   return hipGetLastError();
 }
 
