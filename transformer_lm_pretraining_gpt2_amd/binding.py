@@ -73,10 +73,11 @@ def lib():
     if _lib is None:
         import torch  # noqa: F401  (must precede the CDLL below)
 
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+        path = os.environ.get("GPT2MI_LIBRARY", LIB_PATH)  # another build of the same library, if given
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
                                "(make -C transformer_lm_pretraining_gpt2_amd/csrc)")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         for name, res, args in SIGNATURES:
             f = getattr(L, name)
             f.restype = res
