@@ -423,11 +423,13 @@ __global__ void __launch_bounds__(64) dwte_run_kernel(const float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Fused softmax cross-entropy, one block (1024 threads) per row.  The row is
-// read once into registers; max and sum of exp run over the real vocabulary
-// [0, V); loss = logsumexp - z[target]; the logits are overwritten in place
-// with dscale * (softmax - onehot) on [0, V) and 0 on the padded columns.
-// Probabilities are never stored.
+// Fused softmax cross-entropy, one block (1024 threads) per row, one pass over
+// the logits.  Each thread holds its share of the row, takes its own maximum
+// m_t and keeps e = exp(z - m_t) for its elements (one exponential per
+// logit); one block reduction combines the (m_t, sum e) pairs into
+// logsumexp over the real vocabulary [0, V).  loss = logsumexp - z[target];
+// the logits are overwritten in place with dscale * (softmax - onehot), where
+// softmax = e * exp(m_t - logsumexp), and 0 on the padded columns.
 // ---------------------------------------------------------------------------
 constexpr int CE_T = 1024;
 
@@ -436,7 +438,7 @@ __global__ void __launch_bounds__(CE_T) ce_kernel(T* __restrict__ logits, const 
                                                   float* __restrict__ row_loss, int V, int Vp, float dscale,
                                                   int write_grad) {
   typedef typename Frag<T>::type F;
-  __shared__ float red[CE_T / 64];
+  __shared__ float rm[CE_T / 64], rs[CE_T / 64];
   __shared__ float zt;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int64_t row = blockIdx.x;
@@ -444,53 +446,68 @@ __global__ void __launch_bounds__(CE_T) ce_kernel(T* __restrict__ logits, const 
   const int nvec = Vp / 8;
   const int y = min(max(tgt[row], 0), V - 1);  // out-of-range targets were flagged by the embedding pass
   if (tid == 0) zt = to_f<T>(z[y]);
-  F v[NV];
-  float mx = -INFINITY;
+  constexpr float L2E = 1.4426950408889634f;
+  // load this thread's vectors; columns >= V count as -inf
+  f32x8 e[NV];
+  float mt = -INFINITY;
 #pragma unroll
   for (int k = 0; k < NV; k++) {
     const int vi = tid + k * CE_T;
     if (vi < nvec) {
-      v[k] = ld8(z + vi * 8);
+      const F v = ld8(z + vi * 8);
 #pragma unroll
-      for (int e = 0; e < 8; e++)
-        if (vi * 8 + e < V) mx = fmaxf(mx, to_f<T>(v[k][e]));
+      for (int q = 0; q < 8; q++) e[k][q] = to_f<T>(v[q]);
+      if (vi * 8 + 8 > V) {
+#pragma unroll
+        for (int q = 0; q < 8; q++)
+          if (vi * 8 + q >= V) e[k][q] = -INFINITY;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; q++) mt = fmaxf(mt, e[k][q]);
     }
   }
-  mx = wave_max(mx);
-  if (lane == 0) red[w] = mx;
-  __syncthreads();
-  mx = red[0];
-#pragma unroll
-  for (int i = 1; i < CE_T / 64; i++) mx = fmaxf(mx, red[i]);
-  __syncthreads();
-  float s = 0.f;
+  // e = exp(z - m_t) and its sum (a thread without real columns keeps m_t = -inf, st = 0)
+  float st = 0.f;
+  const float mtl = mt == -INFINITY ? 0.f : mt * L2E;
 #pragma unroll
   for (int k = 0; k < NV; k++) {
     const int vi = tid + k * CE_T;
-    if (vi < nvec)
+    if (vi < nvec) {
 #pragma unroll
-      for (int e = 0; e < 8; e++)
-        if (vi * 8 + e < V) s += __expf(to_f<T>(v[k][e]) - mx);
+      for (int q = 0; q < 8; q++) {
+        e[k][q] = __builtin_amdgcn_exp2f(fmaf(e[k][q], L2E, -mtl));
+        st += e[k][q];
+      }
+    }
   }
-  s = wave_sum(s);
-  if (lane == 0) red[w] = s;
+  // combine (m_t, st) over the block: M = max m_t, S = sum st * exp(m_t - M)
+  float M = wave_max(mt);
+  if (lane == 0) rm[w] = M;
   __syncthreads();
-  s = red[0];
+  M = rm[0];
 #pragma unroll
-  for (int i = 1; i < CE_T / 64; i++) s += red[i];
-  const float lse = mx + __logf(s);
+  for (int i = 1; i < CE_T / 64; i++) M = fmaxf(M, rm[i]);
+  float sc = st > 0.f ? st * __builtin_amdgcn_exp2f((mt - M) * L2E) : 0.f;
+  sc = wave_sum(sc);
+  if (lane == 0) rs[w] = sc;
+  __syncthreads();
+  float S = rs[0];
+#pragma unroll
+  for (int i = 1; i < CE_T / 64; i++) S += rs[i];
+  const float lse = M + __logf(S);
   if (tid == 0) row_loss[row] = lse - zt;
   if (!write_grad) return;
+  const float f = st > 0.f ? __builtin_amdgcn_exp2f((mt - lse) * L2E) * dscale : 0.f;
 #pragma unroll
   for (int k = 0; k < NV; k++) {
     const int vi = tid + k * CE_T;
     if (vi < nvec) {
       F o;
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const int j = vi * 8 + e;
-        const float g = j < V ? (__expf(to_f<T>(v[k][e]) - lse) - (j == y ? 1.f : 0.f)) * dscale : 0.f;
-        o[e] = from_f<T>(g);
+      for (int q = 0; q < 8; q++) {
+        float g = e[k][q] * f;
+        if (vi * 8 + q == y) g -= dscale;
+        o[q] = from_f<T>(g);
       }
       st8(z + vi * 8, o);
     }
@@ -721,6 +738,8 @@ hipError_t cross_entropy(hipStream_t st, Prec p, void* logits, const int32_t* tg
     CE_LAUNCH(TT, 2);       \
   else if (nv <= 4)         \
     CE_LAUNCH(TT, 4);       \
+  else if (nv <= 7)         \
+    CE_LAUNCH(TT, 7);       \
   else if (nv <= 8)         \
     CE_LAUNCH(TT, 8);       \
   else                      \
