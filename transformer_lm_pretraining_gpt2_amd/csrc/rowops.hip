@@ -582,6 +582,8 @@ __global__ void __launch_bounds__(256) norm_final_kernel(const double* __restric
 }
 
 // AdamW with bias correction and decoupled weight decay on indices < n_decay.
+// One 4-element quad per thread; parameters, gradients and moments stream
+// through once, so their loads and stores are marked non-temporal.
 __global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ p, const float* __restrict__ g,
                                                     float* __restrict__ m, float* __restrict__ v,
                                                     bf16* __restrict__ p_lp, int64_t nq, int64_t n_decay, float lr,
@@ -591,10 +593,10 @@ __global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ p, const
   const float sc = *scale;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nq; q += (int64_t)gridDim.x * blockDim.x) {
     const int64_t i = 4 * q;
-    f32x4 pp = *reinterpret_cast<const f32x4*>(p + i);
-    const f32x4 gg = *reinterpret_cast<const f32x4*>(g + i);
-    f32x4 mm = *reinterpret_cast<const f32x4*>(m + i);
-    f32x4 vv = *reinterpret_cast<const f32x4*>(v + i);
+    f32x4 pp = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + i));
+    const f32x4 gg = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + i));
+    f32x4 mm = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(m + i));
+    f32x4 vv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(v + i));
     const float d = i < n_decay ? wd : 0.f;
 #pragma unroll
     for (int e = 0; e < 4; e++) {
@@ -604,9 +606,9 @@ __global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ p, const
       const float mh = mm[e] * rbc1, vh = vv[e] * rbc2;
       pp[e] -= lr * (mh / (sqrtf(vh) + eps) + d * pp[e]);
     }
-    *reinterpret_cast<f32x4*>(p + i) = pp;
-    *reinterpret_cast<f32x4*>(m + i) = mm;
-    *reinterpret_cast<f32x4*>(v + i) = vv;
+    __builtin_nontemporal_store(pp, reinterpret_cast<f32x4*>(p + i));
+    __builtin_nontemporal_store(mm, reinterpret_cast<f32x4*>(m + i));
+    __builtin_nontemporal_store(vv, reinterpret_cast<f32x4*>(v + i));
     if (p_lp) {
       bf16x4 o;
 #pragma unroll
@@ -773,7 +775,7 @@ hipError_t adamw(hipStream_t st, float* p, const float* g, float* m, float* v, v
                  const int* flags) {
   if (n % 4 != 0 || n_decay % 4 != 0) return hipErrorInvalidValue;
   const int64_t nq = n / 4;
-  const unsigned blocks = (unsigned)std::min<int64_t>((nq + 255) / 256, 8192);
+  const unsigned blocks = (unsigned)std::min<int64_t>((nq + 255) / 256, 1 << 30);
   hipLaunchKernelGGL(adamw_kernel, dim3(blocks), dim3(256), 0, st, p, g, m, v, static_cast<bf16*>(p_lp), nq, n_decay, lr,
                      b1, b2, eps, wd, 1.f / bc1, 1.f / bc2, scale, flags);
   return hipGetLastError();
