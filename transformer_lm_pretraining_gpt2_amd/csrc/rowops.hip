@@ -199,7 +199,7 @@ __global__ void __launch_bounds__(RED_THREADS) reduce_jobs_kernel(ReduceJobs job
     f32x4 v[RED_SLICES];
 #pragma unroll
     for (int p = 0; p < RED_SLICES; p++)
-      if (p < J.nparts) v[p] = ld4(src + p * J.ld);
+      if (p < J.nparts) v[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + p * J.ld));
     f32x4 t = v[0];
 #pragma unroll
     for (int p = 1; p < RED_SLICES; p++)
@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(RED_THREADS) reduce_jobs_kernel(ReduceJobs job
     const int p0 = (int)((int64_t)J.nparts * slice / RED_SLICES), p1 = (int)((int64_t)J.nparts * (slice + 1) / RED_SLICES);
     f32x4 t = {0.f, 0.f, 0.f, 0.f};
     if (j < J.n)
-      for (int p = p0; p < p1; p++) t += ld4(J.part + (int64_t)p * J.ld + j);
+      for (int p = p0; p < p1; p++) t += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(J.part + (int64_t)p * J.ld + j));
     sh[tid] = t;
     __syncthreads();
     if (slice == 0 && j < J.n) {
@@ -454,7 +454,7 @@ __global__ void __launch_bounds__(CE_T) ce_kernel(T* __restrict__ logits, const 
   for (int k = 0; k < NV; k++) {
     const int vi = tid + k * CE_T;
     if (vi < nvec) {
-      const F v = ld8(z + vi * 8);
+      const F v = __builtin_nontemporal_load(reinterpret_cast<const F*>(z + vi * 8));
 #pragma unroll
       for (int q = 0; q < 8; q++) e[k][q] = to_f<T>(v[q]);
       if (vi * 8 + 8 > V) {
@@ -509,7 +509,7 @@ __global__ void __launch_bounds__(CE_T) ce_kernel(T* __restrict__ logits, const 
         if (vi * 8 + q == y) g -= dscale;
         o[q] = from_f<T>(g);
       }
-      st8(z + vi * 8, o);
+      __builtin_nontemporal_store(o, reinterpret_cast<F*>(z + vi * 8));
     }
   }
 }
@@ -547,7 +547,7 @@ __global__ void __launch_bounds__(256) norm_part_kernel(const float* __restrict_
   const int64_t q0 = blockIdx.x * per, q1 = min(nq, q0 + per);
   double s = 0.0;
   for (int64_t q = q0 + tid; q < q1; q += 256) {
-    const f32x4 v = *reinterpret_cast<const f32x4*>(g + 4 * q);
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + 4 * q));
     s += (double)v[0] * v[0] + (double)v[1] * v[1] + (double)v[2] * v[2] + (double)v[3] * v[3];
   }
   if (blockIdx.x == gridDim.x - 1)
