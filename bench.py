@@ -31,9 +31,13 @@ DOMINANT = {"gpt2_124m": "gemm_tn_f32"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash():
+# the sources each measured kernel is built from (its counters go stale when they change)
+KERNEL_SOURCES = {"gemm_tn_f32": ("gemm.hip", "common.h"), "attn_bwd_dkv": ("attention.hip", "common.h")}
+
+
+def kernel_source_hash(kernel="gemm_tn_f32"):
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h"):
+    for f in KERNEL_SOURCES.get(kernel, ("gemm.hip", "attention.hip", "rowops.hip", "common.h")):
         with open(os.path.join(ROOT, "transformer_lm_pretraining_gpt2_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -49,7 +53,7 @@ def measured_traffic(kernel, workload):
     except (OSError, ValueError):
         return None
     e = d.get(workload, {}).get(kernel)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
 

@@ -19,13 +19,14 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# kernel id -> mangled-name fragment of the instantiation it launches for the
-# GPT-2 124M bf16 workload
+# kernel id -> mangled-name fragments of the instantiations it launches for
+# the GPT-2 124M bf16 workload (a launch of any of them counts as one launch)
 KERNELS = {
-    "gemm_tn_f32": "gemm_kernelIDF16bLi256ELi192ELi64ELi2ELi2ELi1ELi1ELi4E",
-    "gemm_nt_store": "gemm_kernelIDF16bLi256ELi192ELi64ELi2ELi2ELi0ELi0ELi0E",
-    "gemm_nn_store": "gemm_kernelIDF16bLi256ELi192ELi64ELi2ELi2ELi0ELi1ELi0E",
-    "attn_bwd_dkv": "attn_dkv_kernelIDF16bLi64E",
+    # weight gradients of the four per-layer linears: 128x128 tiles (qkv, fc,
+    # fcproj) and the 256x192 tile (attention projection)
+    "gemm_tn_f32": ["gemm_kernelIDF16bLi128ELi128ELi64ELi2ELi2ELi1ELi1ELi4E",
+                    "gemm_kernelIDF16bLi256ELi192ELi64ELi2ELi2ELi1ELi1ELi4E"],
+    "attn_bwd_dkv": ["attn_dkv_kernelIDF16bLi64E"],
 }
 COPY = "copyBuffer"  # the runtime's device-to-device copy kernel, used by dst.copy_(src)
 
@@ -40,10 +41,10 @@ def read(path, counter):
     return out, by_id
 
 
-def per_dispatch(rows, frag):
-    vals = [v for name, vs in rows.items() if frag in name for v in vs]
+def per_dispatch(rows, frags):
+    vals = [v for name, vs in rows.items() if any(f in name for f in frags) for v in vs]
     if not vals:
-        raise SystemExit(f"no dispatch matching {frag}")
+        raise SystemExit(f"no dispatch matching {frags}")
     return sum(vals) / len(vals), len(vals)
 
 
@@ -77,7 +78,7 @@ def main(argv=None):
         "fetch_kib_raw": kf, "write_kib_raw": kw, "dispatches": [nf, nw],
         "copy_mib": a.copy_mib, "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
         "fetch_scale": f_scale, "write_scale": w_scale,
-        "source_hash": kernel_source_hash(),
+        "source_hash": kernel_source_hash(a.kernel),
     }
     d = json.load(open(a.out)) if os.path.exists(a.out) else {}
     d.setdefault(a.workload, {})[a.kernel] = entry
