@@ -73,9 +73,9 @@ __device__ __forceinline__ float gelu_sigmoid(float x) {
   return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z2));
 }
 __device__ __forceinline__ float gelu_tanh(float x) { return x * gelu_sigmoid(x); }
-__device__ __forceinline__ float gelu_tanh_grad(float x) {
+// gelu'(x) from the same sigmoid s = gelu_sigmoid(x)
+__device__ __forceinline__ float gelu_tanh_grad_s(float x, float s) {
   const float k = 2.f * 0.7978845608028654f;
-  const float s = gelu_sigmoid(x);
   return s + x * s * (1.f - s) * k * (1.f + 3.f * 0.044715f * x * x);
 }
 

@@ -315,11 +315,14 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
         for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e]);
         st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
       } else if constexpr (EPI == EPI_GELU) {
+        // the backward needs only gelu' at the pre-activation: store that
+        // (from the fp32 value) next to the activation
         F u, o;
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-          u[e] = from_f<T>(v[e]);
-          o[e] = from_f<T>(gelu_tanh(v[e]));
+          const float sg = gelu_sigmoid(v[e]);
+          u[e] = from_f<T>(gelu_tanh_grad_s(v[e], sg));
+          o[e] = from_f<T>(v[e] * sg);
         }
         st8(static_cast<T*>(g.aux) + (int64_t)i * g.ldaux + j, u);
         st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
@@ -330,7 +333,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
         const F u = ld8(static_cast<const T*>(g.aux) + (int64_t)i * g.ldaux + j);
         F o;
 #pragma unroll
-        for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e] * gelu_tanh_grad(to_f<T>(u[e])));
+        for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e] * to_f<T>(u[e]));
         st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
       } else {  // EPI_F32
         float* Cp = static_cast<float*>(g.C) + (int64_t)blockIdx.y * g.split_stride + (int64_t)i * g.ldc + j;

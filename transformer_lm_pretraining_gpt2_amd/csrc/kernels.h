@@ -11,9 +11,9 @@ enum Prec { F32 = 0, BF16 = 1 };
 // A(i, r) = A[i*lda + r] (a_t = 0) or A[r*lda + i] (a_t = 1); same for B.
 enum Epi {
   EPI_STORE = 0,    // out (act type) = acc + bias[j]
-  EPI_GELU = 1,     // aux = acc + bias[j]; out = gelu_tanh(aux)           (act type)
+  EPI_GELU = 1,     // u = acc + bias[j]; out = gelu_tanh(u), aux = gelu_tanh'(u)   (act type)
   EPI_RESID = 2,    // out (fp32) = resid (fp32) + acc + bias[j]
-  EPI_GELU_BWD = 3, // out (act type) = acc * gelu_tanh'(aux)
+  EPI_GELU_BWD = 3, // out (act type) = acc * aux   (aux = gelu_tanh' at the pre-activation)
   EPI_F32 = 4       // out (fp32) = (accumulate ? out : 0) + acc; split s writes out + s*split_stride
 };
 
