@@ -213,39 +213,15 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const T* __restric
 }
 
 // ------------------------------------------------------------------------
-// D[b,h,i] = sum_d dout[i, h*hd + d] * out[i, h*hd + d]
-// ------------------------------------------------------------------------
-template <typename T, int HD>
-__global__ void attn_dsum_kernel(const T* __restrict__ out, const T* __restrict__ dout, float* __restrict__ dsum, int T_,
-                                 int NH, int64_t n) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= n) return;
-  const int h = idx % NH;
-  const int64_t row = idx / NH;  // b*T + t
-  const int C = NH * HD;
-  const T* o = out + row * C + h * HD;
-  const T* d = dout + row * C + h * HD;
-  float s = 0.f;
-#pragma unroll 2
-  for (int k = 0; k < HD; k += 8) {
-    const auto a = ld8(o + k);
-    const auto c = ld8(d + k);
-#pragma unroll
-    for (int e = 0; e < 8; e++) s += to_f<T>(a[e]) * to_f<T>(c[e]);
-  }
-  const int64_t b = row / T_, t = row % T_;
-  dsum[(b * NH + h) * T_ + t] = s;
-}
-
-// ------------------------------------------------------------------------
 // dQ.  grid (ceil(T/128), NH, B).  Per query column (one per lane):
+// D = rowsum(dO * O) (stored for the dK/dV kernel, which runs after this one),
 // P^T = exp(S^T - LSE), dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ = scale dS K.
 // Per key tile: K and V rows; K^T fragments come from transposing reads.
 // ------------------------------------------------------------------------
 template <typename T, int HD>
-__global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
-                                                             const float* __restrict__ lse,
-                                                             const float* __restrict__ dsum, T* __restrict__ dqkv,
+__global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict__ qkv, const T* __restrict__ out,
+                                                             const T* __restrict__ dout, const float* __restrict__ lse,
+                                                             float* __restrict__ dsum, T* __restrict__ dqkv,
                                                              int T_, int NH, float sl2, float scale) {
   typedef RowTile<T, HD> RT;
   constexpr int LD = RT::LD, ND = HD / 16, NDT = HD / 32;
@@ -268,13 +244,21 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
   F qf[ND], df[ND];
   float lse2 = 0.f, dq_d = 0.f;
   if (active) {
+    // the lane pair (l, l^32) holds the query's dO row: each half dots its
+    // 8-element slices with O, in slice order, then the halves are added
+    float part = 0.f;
 #pragma unroll
     for (int ds = 0; ds < ND; ds++) {
       qf[ds] = ld8(base + (int64_t)q * S3 + h * HD + ds * 16 + 8 * lg);
       df[ds] = ld8(dout + ((int64_t)b * T_ + q) * C + h * HD + ds * 16 + 8 * lg);
+      const F of = ld8(out + ((int64_t)b * T_ + q) * C + h * HD + ds * 16 + 8 * lg);
+#pragma unroll
+      for (int e = 0; e < 8; e++) part = fmaf(to_f<T>(df[ds][e]), to_f<T>(of[e]), part);
     }
+    const float other = __shfl_xor(part, 32, 64);
+    dq_d = lg == 0 ? part + other : other + part;
     lse2 = lse[((int64_t)b * NH + h) * T_ + q] * LOG2E;
-    dq_d = dsum[((int64_t)b * NH + h) * T_ + q];
+    if (lg == 0) dsum[((int64_t)b * NH + h) * T_ + q] = dq_d;
   }
   f32x16 dq[NDT];
 #pragma unroll
@@ -495,24 +479,23 @@ hipError_t fwd_t(hipStream_t st, const void* qkv, void* out, float* lse, int B, 
 }
 
 template <typename T, int HD>
-hipError_t dsum_t(hipStream_t st, const void* out, const void* dout, float* dsum, int B, int T_, int NH) {
-  const int64_t n = (int64_t)B * T_ * NH;
-  hipLaunchKernelGGL((attn_dsum_kernel<T, HD>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                     static_cast<const T*>(out), static_cast<const T*>(dout), dsum, T_, NH, n);
+hipError_t dq_t(hipStream_t st, const void* qkv, const void* out, const void* dout, const float* lse, float* dsum,
+                void* dqkv, int B, int T_, int NH) {
+  dim3 grid((T_ + NW * WQ - 1) / (NW * WQ), NH, B);
+  const float scale = 1.f / sqrtf((float)HD), sl2 = LOG2E * scale;
+  hipLaunchKernelGGL((attn_dq_kernel<T, HD>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(qkv),
+                     static_cast<const T*>(out), static_cast<const T*>(dout), lse, dsum, static_cast<T*>(dqkv), T_, NH,
+                     sl2, scale);
   return hipGetLastError();
 }
 
-template <typename T, int HD, bool DQ>
-hipError_t bwd_t(hipStream_t st, const void* qkv, const void* dout, const float* lse, const float* dsum, void* dqkv,
+template <typename T, int HD>
+hipError_t dkv_t(hipStream_t st, const void* qkv, const void* dout, const float* lse, const float* dsum, void* dqkv,
                  int B, int T_, int NH) {
   dim3 grid((T_ + NW * WQ - 1) / (NW * WQ), NH, B);
   const float scale = 1.f / sqrtf((float)HD), sl2 = LOG2E * scale;
-  if (DQ)
-    hipLaunchKernelGGL((attn_dq_kernel<T, HD>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(qkv),
-                       static_cast<const T*>(dout), lse, dsum, static_cast<T*>(dqkv), T_, NH, sl2, scale);
-  else
-    hipLaunchKernelGGL((attn_dkv_kernel<T, HD>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(qkv),
-                       static_cast<const T*>(dout), lse, dsum, static_cast<T*>(dqkv), T_, NH, sl2, scale);
+  hipLaunchKernelGGL((attn_dkv_kernel<T, HD>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(qkv),
+                     static_cast<const T*>(dout), lse, dsum, static_cast<T*>(dqkv), T_, NH, sl2, scale);
   return hipGetLastError();
 }
 
@@ -530,38 +513,30 @@ hipError_t attn_fwd(hipStream_t st, Prec p, const void* qkv, void* out, float* l
   return hipErrorInvalidValue;
 }
 
-hipError_t attn_bwd_dsum(hipStream_t st, Prec p, const void* out, const void* dout, float* dsum, int B, int T_, int NH,
-                         int hd) {
-  if (p == BF16) {
-    if (hd == 64) return dsum_t<bf16, 64>(st, out, dout, dsum, B, T_, NH);
-    if (hd == 32) return dsum_t<bf16, 32>(st, out, dout, dsum, B, T_, NH);
-  } else {
-    if (hd == 64) return dsum_t<float, 64>(st, out, dout, dsum, B, T_, NH);
-    if (hd == 32) return dsum_t<float, 32>(st, out, dout, dsum, B, T_, NH);
-  }
+#define ATTN_HD_DISPATCH(CALL)                            \
+  if (T_ % KT != 0) return hipErrorInvalidValue;           \
+  if (p == BF16) {                                         \
+    if (hd == 64) return CALL(bf16, 64);                   \
+    if (hd == 32) return CALL(bf16, 32);                   \
+  } else {                                                 \
+    if (hd == 64) return CALL(float, 64);                  \
+    if (hd == 32) return CALL(float, 32);                  \
+  }                                                        \
   return hipErrorInvalidValue;
-}
 
-#define ATTN_BWD_DISPATCH(DQ)                                                                   \
-  if (T_ % KT != 0) return hipErrorInvalidValue;                                                \
-  if (p == BF16) {                                                                              \
-    if (hd == 64) return bwd_t<bf16, 64, DQ>(st, qkv, dout, lse, dsum, dqkv, B, T_, NH);        \
-    if (hd == 32) return bwd_t<bf16, 32, DQ>(st, qkv, dout, lse, dsum, dqkv, B, T_, NH);        \
-  } else {                                                                                      \
-    if (hd == 64) return bwd_t<float, 64, DQ>(st, qkv, dout, lse, dsum, dqkv, B, T_, NH);       \
-    if (hd == 32) return bwd_t<float, 32, DQ>(st, qkv, dout, lse, dsum, dqkv, B, T_, NH);       \
-  }                                                                                             \
-  return hipErrorInvalidValue;
+hipError_t attn_bwd_dq(hipStream_t st, Prec p, const void* qkv, const void* out, const void* dout, const float* lse,
+                       float* dsum, void* dqkv, int B, int T_, int NH, int hd) {
+#define DQ_CALL(TT, H) dq_t<TT, H>(st, qkv, out, dout, lse, dsum, dqkv, B, T_, NH)
+  ATTN_HD_DISPATCH(DQ_CALL)
+#undef DQ_CALL
+}
 
 hipError_t attn_bwd_dkv(hipStream_t st, Prec p, const void* qkv, const void* dout, const float* lse, const float* dsum,
                         void* dqkv, int B, int T_, int NH, int hd) {
-  ATTN_BWD_DISPATCH(false)
+#define DKV_CALL(TT, H) dkv_t<TT, H>(st, qkv, dout, lse, dsum, dqkv, B, T_, NH)
+  ATTN_HD_DISPATCH(DKV_CALL)
+#undef DKV_CALL
 }
-
-hipError_t attn_bwd_dq(hipStream_t st, Prec p, const void* qkv, const void* dout, const float* lse, const float* dsum,
-                       void* dqkv, int B, int T_, int NH, int hd) {
-  ATTN_BWD_DISPATCH(true)
-}
-#undef ATTN_BWD_DISPATCH
+#undef ATTN_HD_DISPATCH
 
 }  // namespace gpt2k

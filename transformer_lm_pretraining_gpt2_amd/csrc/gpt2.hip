@@ -656,23 +656,21 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "proj dx"))) return rc;
     // attention
     {
+      // dQ first: it also stores D = rowsum(dO * O), which dK/dV reads
       const double pairs = (double)h->B * NH * ((double)h->T * (h->T + 1) / 2);
-      rc = hip_check(h, attn_bwd_dsum(h->st, h->prec, h->w<void>(P.atty[l]), h->w<void>(P.datty), h->w<float>(P.dsum),
-                                      h->B, h->T, NH, hd),
-                     "attn dsum");
+      {
+        Timer t(h, K_ATTN_DQ, 4.0 * hd * pairs);
+        rc = hip_check(h, attn_bwd_dq(h->st, h->prec, h->w<void>(P.qkv[l]), h->w<void>(P.atty[l]), h->w<void>(P.datty),
+                                      h->w<float>(P.lse[l]), h->w<float>(P.dsum), h->w<void>(P.dqkv), h->B, h->T, NH,
+                                      hd),
+                       "attn dq");
+      }
       if (rc) return rc;
       {
         Timer t(h, K_ATTN_DKV, 4.0 * hd * pairs);
         rc = hip_check(h, attn_bwd_dkv(h->st, h->prec, h->w<void>(P.qkv[l]), h->w<void>(P.datty), h->w<float>(P.lse[l]),
                                        h->w<float>(P.dsum), h->w<void>(P.dqkv), h->B, h->T, NH, hd),
                        "attn dkv");
-      }
-      if (rc) return rc;
-      {
-        Timer t(h, K_ATTN_DQ, 4.0 * hd * pairs);
-        rc = hip_check(h, attn_bwd_dq(h->st, h->prec, h->w<void>(P.qkv[l]), h->w<void>(P.datty), h->w<float>(P.lse[l]),
-                                      h->w<float>(P.dsum), h->w<void>(P.dqkv), h->B, h->T, NH, hd),
-                       "attn dq");
       }
       if (rc) return rc;
     }

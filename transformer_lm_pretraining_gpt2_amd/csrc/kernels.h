@@ -47,13 +47,12 @@ int gemm_split_hint(Prec p, int a_t, int b_t, int M, int N, int K);
 
 // ---- attention (causal, packed qkv [B*T, 3C]: q heads | k heads | v heads) ----
 hipError_t attn_fwd(hipStream_t st, Prec p, const void* qkv, void* out, float* lse, int B, int T, int NH, int hd);
-// backward in three launches: D = rowsum(dout * out); dK,dV; dQ
-hipError_t attn_bwd_dsum(hipStream_t st, Prec p, const void* out, const void* dout, float* dsum, int B, int T, int NH,
-                         int hd);
+// backward in two launches: dQ (which also stores D = rowsum(dout * out) in
+// dsum [B, NH, T]), then dK,dV (which reads D)
+hipError_t attn_bwd_dq(hipStream_t st, Prec p, const void* qkv, const void* out, const void* dout, const float* lse,
+                       float* dsum, void* dqkv, int B, int T, int NH, int hd);
 hipError_t attn_bwd_dkv(hipStream_t st, Prec p, const void* qkv, const void* dout, const float* lse, const float* dsum,
                         void* dqkv, int B, int T, int NH, int hd);
-hipError_t attn_bwd_dq(hipStream_t st, Prec p, const void* qkv, const void* dout, const float* lse, const float* dsum,
-                       void* dqkv, int B, int T, int NH, int hd);
 
 // ---- LayerNorm ----
 hipError_t layernorm_fwd(hipStream_t st, Prec p, const float* x, const float* g, const float* b, void* y, float* mean,
