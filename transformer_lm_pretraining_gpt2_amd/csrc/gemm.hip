@@ -344,9 +344,8 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   }
 }
 
-template <typename T, int BM, int BN, int WI, int WJ, int AT, int BT, int EPI>
+template <typename T, int BM, int BN, int WI, int WJ, int AT, int BT, int EPI, int BK>
 hipError_t launch(hipStream_t st, const GemmArgs& g) {
-  constexpr int BK = sizeof(T) == 2 ? 64 : 32;
   constexpr int VE = Vec16<T>::n;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.K <= 0 || g.splits < 1 || g.K % (g.splits * BK) != 0 || g.M % VE != 0 || g.N % 8 != 0 || g.lda % VE != 0 ||
@@ -359,35 +358,51 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
   return hipGetLastError();
 }
 
-// Tile shape per operand layout and product shape (bf16), from a sweep of the
-// step's matmuls on MI355X.  The 128x128 tile runs two blocks per CU (two
-// waves per SIMD), which hides one block's prologue and epilogue behind the
-// other's main loop; it wins wherever the product is small.  The 8-wave
-// 256x256 tile (also two waves per SIMD, twice the operand reuse) wins on long
-// reductions and large outputs, and on the tied output layer's weight
-// gradient; the 4-wave 256x192 tile only on the smallest weight gradient.
-enum TileKind { TILE_128 = 0, TILE_256x192 = 1, TILE_256_W8 = 2 };
+// Tile shape and reduction step per operand layout and product shape (bf16),
+// from sweeps of the step's matmuls on MI355X.
+//  * 128x128, 4 waves of 64x64: two or three blocks per CU hide one block's
+//    prologue and epilogue behind the others' main loops; best for small
+//    products and short reductions.  With BK = 32 (41 KB of LDS, three
+//    blocks per CU) it is the weight-gradient tile.
+//  * 8 waves, 256x256 (waves of 128x64, two per SIMD, twice the operand
+//    reuse): large outputs with short reductions (MLP up-projection, tied
+//    head forward and weight gradient).
+//  * 4 waves, 256x192, BK = 32: long reductions with a 768-wide output
+//    (MLP down-projection, input gradients of fc/qkv/tied head) and the
+//    smallest weight gradient.
+enum TileKind { TILE_128 = 0, TILE_128_K32, TILE_256x192_K32, TILE_256_W8, TILE_256_W8_K32 };
 
 TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
   if (p != BF16 || M < 256) return TILE_128;
   const int64_t mn = (int64_t)M * N;
   if (a_t && b_t) {
-    if (mn >= 8000000) return TILE_256_W8;
-    if (mn <= 1000000 && N % 192 == 0) return TILE_256x192;
-    return TILE_128;
+    if (mn >= 8000000) return TILE_256_W8_K32;
+    if (mn <= 1000000 && N % 192 == 0) return TILE_256x192_K32;
+    return TILE_128_K32;
   }
+  if (K >= 2048 && N % 192 == 0) return TILE_256x192_K32;
   if (K >= 2048 || mn >= 40000000) return TILE_256_W8;
   return TILE_128;
+}
+
+int tile_bk(Prec p, TileKind k) {
+  if (p != BF16) return 32;
+  return (k == TILE_128 || k == TILE_256_W8) ? 64 : 32;
 }
 
 template <typename T, int AT, int BT, int EPI>
 hipError_t launch_tiled(hipStream_t st, const GemmArgs& g, TileKind k) {
   if constexpr (sizeof(T) == 2) {
-    if (k == TILE_256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI>(st, g);
-    if constexpr (AT == 1)
-      if (k == TILE_256x192) return launch<T, 256, 192, 2, 2, AT, BT, EPI>(st, g);
+    if (k == TILE_256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI, 64>(st, g);
+    if (k == TILE_256x192_K32) return launch<T, 256, 192, 2, 2, AT, BT, EPI, 32>(st, g);
+    if constexpr (AT == 1) {
+      if (k == TILE_256_W8_K32) return launch<T, 256, 256, 2, 4, AT, BT, EPI, 32>(st, g);
+      if (k == TILE_128_K32) return launch<T, 128, 128, 2, 2, AT, BT, EPI, 32>(st, g);
+    }
+    return launch<T, 128, 128, 2, 2, AT, BT, EPI, 64>(st, g);
+  } else {
+    return launch<T, 128, 128, 2, 2, AT, BT, EPI, 32>(st, g);
   }
-  return launch<T, 128, 128, 2, 2, AT, BT, EPI>(st, g);
 }
 
 template <typename T>
@@ -409,18 +424,20 @@ hipError_t dispatch(hipStream_t st, int a_t, int b_t, int epi, const GemmArgs& g
 
 hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArgs& g) {
   TileKind k = choose_tile(p, a_t, b_t, g.M, g.N, g.K);
-  if (k == TILE_256_W8 && g.colsum) k = TILE_256x192;  // the 8-wave tile has no bias-gradient path
+  if ((k == TILE_256_W8 || k == TILE_256_W8_K32) && g.colsum)
+    k = TILE_256x192_K32;  // the 8-wave tile has no bias-gradient path
   return p == BF16 ? dispatch<bf16>(st, a_t, b_t, epi, g, k) : dispatch<float>(st, a_t, b_t, epi, g, k);
 }
 
 int gemm_split_hint(Prec p, int a_t, int b_t, int M, int N, int K) {
   const TileKind k = choose_tile(p, a_t, b_t, M, N, K);
-  const int bm = k == TILE_128 ? 128 : 256, bn = k == TILE_256x192 ? 192 : (k == TILE_256_W8 ? 256 : 128);
-  const int bk = p == BF16 ? 64 : 32;
+  const int bm = (k == TILE_128 || k == TILE_128_K32) ? 128 : 256;
+  const int bn = k == TILE_256x192_K32 ? 192 : (k == TILE_256_W8 || k == TILE_256_W8_K32) ? 256 : 128;
+  const int bk = tile_bk(p, k);
   const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   // one block per CU for the large tiles, two for 128x128; the reduction must
   // split into equal multiples of the K step
-  const int target = k == TILE_128 ? 512 : 256;
+  const int target = (k == TILE_128 || k == TILE_128_K32) ? 512 : 256;
   int s = 1;
   while (s < 16 && tiles * s < target && K % (2 * s * bk) == 0) s *= 2;
   return s;

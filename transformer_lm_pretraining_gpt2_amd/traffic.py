@@ -23,9 +23,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # the GPT-2 124M bf16 workload (a launch of any of them counts as one launch)
 KERNELS = {
     # weight gradients of the four per-layer linears: 128x128 tiles (qkv, fc,
-    # fcproj) and the 256x192 tile (attention projection)
-    "gemm_tn_f32": ["gemm_kernelIDF16bLi128ELi128ELi64ELi2ELi2ELi1ELi1ELi4E",
-                    "gemm_kernelIDF16bLi256ELi192ELi64ELi2ELi2ELi1ELi1ELi4E"],
+    # fcproj) and the 256x192 tile (attention projection), both BK = 32
+    "gemm_tn_f32": ["gemm_kernelIDF16bLi128ELi128ELi32ELi2ELi2ELi1ELi1ELi4E",
+                    "gemm_kernelIDF16bLi256ELi192ELi32ELi2ELi2ELi1ELi1ELi4E"],
     "attn_bwd_dkv": ["attn_dkv_kernelIDF16bLi64E"],
 }
 COPY = "copyBuffer"  # the runtime's device-to-device copy kernel, used by dst.copy_(src)
