@@ -103,7 +103,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Per key tile: K and V rows (next tile prefetched into registers).
 // ------------------------------------------------------------------------
 template <typename T, int HD>
-__global__ void __launch_bounds__(NW * 64, 2) attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ out,
+__global__ void __launch_bounds__(NW * 64, 4) attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ out,
                                                               float* __restrict__ lse, int T_, int NH, float sl2) {
   typedef RowTile<T, HD> RT;
   constexpr int LD = RT::LD, ND = HD / 16, NDT = HD / 32;
@@ -280,28 +280,31 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
     }
     if (active && kv0 <= q0 + WQ - 1) {
       const bool diag = kv0 + KT - 1 > q0;
-      f32x16 s[2], dp[2];
+      // the tile's two 32-key halves one after the other: one S^T and one
+      // dP^T accumulator live at a time
 #pragma unroll
       for (int c2 = 0; c2 < 2; c2++) {
-        s[c2] = f32x16{};
-        dp[c2] = f32x16{};
+        f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ds = 0; ds < ND; ds++) {
-          mma16(s[c2], ld8(Ks[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), qf[ds]);
-          mma16(dp[c2], ld8(Vs[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), df[ds]);
+          mma16(s, ld8(Ks[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), qf[ds]);
+          mma16(dp, ld8(Vs[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), df[ds]);
         }
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          float p = fast_exp2(fmaf(s[c2][r], sl2, -lse2));
-          if (diag && kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4) > q) p = 0.f;
-          s[c2][r] = p * (dp[c2][r] - dq_d);  // dS^T
+        for (int r = 0; r < 16; r++) s[r] = fast_exp2(fmaf(s[r], sl2, -lse2));
+        if (diag) {  // causal mask: only tiles that straddle this wave's queries
+#pragma unroll
+          for (int r = 0; r < 16; r++)
+            if (kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4) > q) s[r] = 0.f;
         }
-      }
 #pragma unroll
-      for (int c = 0; c < KT / 16; c++) {
-        const F sf = acc_frag<T>(s[c / 2], c % 2);
+        for (int r = 0; r < 16; r++) s[r] = s[r] * (dp[r] - dq_d);  // dS^T
 #pragma unroll
-        for (int dt = 0; dt < NDT; dt++) mma16(dq[dt], ld_tsplit<T, LD>(Ks[cur], dt * 32, c, lane), sf);
+        for (int h2 = 0; h2 < 2; h2++) {
+          const F sf = acc_frag<T>(s, h2);
+#pragma unroll
+          for (int dt = 0; dt < NDT; dt++) mma16(dq[dt], ld_tsplit<T, LD>(Ks[cur], dt * 32, 2 * c2 + h2, lane), sf);
+        }
       }
     }
     if (more) {
