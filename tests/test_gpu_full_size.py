@@ -1,5 +1,7 @@
-"""GPU parity at the full GPT-2 124M size, in the launch configuration the
-throughput benchmark times: bf16, B = 16, T = 1024, random GPT-2 init.
+"""GPU parity at full size, in each workload's own launch configuration: the
+GPT-2 124M step the throughput benchmark times (bf16, B = 16, T = 1024), the
+small and story-scale GPTs at their batch sizes, and GPT-2 350M with gradient
+accumulation; random GPT-2 init.
 
 The oracle cannot run a whole 16 x 1024 batch in reasonable time, so:
   * forward: a batch of 16 distinct Zipf sequences; the per-position losses of
@@ -11,8 +13,11 @@ The oracle cannot run a whole 16 x 1024 batch in reasonable time, so:
     loss, so the oracle's B = 1 step (forward, backward, clip, AdamW) is the
     reference for every gradient, the norm and the updated parameters, while
     the GPU runs every kernel at its full-size shapes and tiles.
-The oracle runs in fp32 here (about 20 s per sequence); its rounding error is
-orders of magnitude below the bf16 tolerances.
+The oracle runs its forward and backward in fp32 here (about 20 s per 124M
+sequence); its rounding error is orders of magnitude below the bf16
+tolerances.  The same repeated-sequence construction covers the other
+configurations (with K = 2 accumulated micro-steps for 350M, whose gradient is
+again that of the single sequence).
 """
 import numpy as np
 import pytest
@@ -67,3 +72,38 @@ def test_full_size_step_repeated_sequence(params):
     g["rows"] = [g["rows"][0][k * T:(k + 1) * T] for k in range(B)]
     o["rows"] = [o["rows"][0]] * B
     compare(MODEL, g, o, "bf16")
+
+
+def _repeated_step(model, B, T, prec, seed, K=1):
+    """GPU step on one sequence repeated B times in each of K micro-steps
+    against the oracle's step on that single sequence (same gradient)."""
+    p0 = synth.init_params(binding.param_layout(model), model.n_layer, model.vocab_size)
+    ids, tgt = batches(model, 1, T, 1, seed=seed)[0]
+    rep = (np.repeat(ids, B, axis=0), np.repeat(tgt, B, axis=0))
+    print(f"gpu step (B={B}, T={T}, K={K}, {prec})", flush=True)
+    g = gpu_step(model, B, T, prec, p0, [rep] * K)
+    print("oracle step (B=1, fp32 forward/backward, fp64 update)", flush=True)
+    o = oracle_step(model, p0, [(ids, tgt)], R=np.float32)
+    g["loss"] = [float(np.mean(g["loss"]))]
+    g["rows"] = [r[k * T:(k + 1) * T] for r in g["rows"] for k in range(B)]
+    o["rows"] = [o["rows"][0]] * (B * K)
+    compare(model, g, o, prec)
+
+
+def test_story_config_launch_shape():
+    # story-scale GPT (27.6M params: V 4096, L 8, nh 8, C 512) at its own B = 64, T = 512
+    rc = CONFIGS["story"]
+    _repeated_step(rc.model, rc.B, rc.T, "bf16", seed=2024)
+
+
+def test_gpt2_350m_launch_shape_with_accumulation():
+    # GPT-2 350M (L 24, nh 16, C 1024) at B = 16, T = 1024 with two accumulated
+    # micro-steps (loss / K, the second adding onto the first)
+    rc = CONFIGS["gpt2_350m"]
+    _repeated_step(rc.model, rc.B, rc.T, "bf16", seed=350, K=2)
+
+
+def test_small_config_launch_shape():
+    # small GPT (V 4096, L 4, nh 4, C 256) at its own B = 64, T = 256
+    rc = CONFIGS["small"]
+    _repeated_step(rc.model, rc.B, rc.T, "bf16", seed=64)
