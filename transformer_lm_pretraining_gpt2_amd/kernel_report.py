@@ -4,22 +4,24 @@ achieved HBM bandwidth, from rocprofv3 runs of the same bench command.
 Inputs (all from `python3 bench.py --steps S --warmup W --no-cpu-baseline
 --copy-mib N` under rocprofv3):
   * a `--kernel-trace --stats` run: per-kernel call counts and durations;
-  * a `--pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE` run: MFMA utilisation
-    per dispatch = sum of SQ_VALU_MFMA_BUSY_CYCLES / (max GRBM_GUI_ACTIVE x
-    SIMDs), the MfmaUtil definition rocprofv3 itself lists;
+  * a `--pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F32` run:
+    MFMA FLOPs executed per dispatch (MOPS x 512, rocprofv3's own MfmaFlops
+    definition; padded or masked tile work included), which over the traced
+    duration and the dense MFMA peak gives the MFMA utilisation;
   * a `--pmc FETCH_SIZE` and a `--pmc WRITE_SIZE` run: HBM bytes per dispatch,
     scaled by what the counters read for the plain N MiB device copy (see
     traffic.py).
 Achieved GB/s = (fetch + write bytes per dispatch) / average traced duration.
 
     python -m transformer_lm_pretraining_gpt2_amd.kernel_report STATS_CSV MFMA_CSV FETCH_CSV WRITE_CSV \\
-        --copy-mib 1024 --steps 7 --simds 1024
+        --copy-mib 1024 --steps 7
 """
 import argparse
 import collections
 import csv
 import re
 
+from transformer_lm_pretraining_gpt2_amd.config import MI355X_BF16_PEAK_FLOPS, MI355X_FP32_MFMA_PEAK_FLOPS
 from transformer_lm_pretraining_gpt2_amd.traffic import COPY, read
 
 
@@ -53,15 +55,16 @@ def main(argv=None):
     ap.add_argument("write_csv")
     ap.add_argument("--copy-mib", type=int, required=True)
     ap.add_argument("--steps", type=float, required=True, help="training steps the traced run executed")
-    ap.add_argument("--simds", type=int, default=1024, help="SIMDs on the device (CUs x 4)")
+    ap.add_argument("--peak-bf16", type=float, default=MI355X_BF16_PEAK_FLOPS)
+    ap.add_argument("--peak-f32", type=float, default=MI355X_FP32_MFMA_PEAK_FLOPS)
     ap.add_argument("--top", type=int, default=30)
     a = ap.parse_args(argv)
 
     stats = list(csv.DictReader(open(a.stats_csv)))
-    mf = collections.defaultdict(list)
+    mf = collections.defaultdict(list)  # executed MFMA work per dispatch, in seconds at peak
     for name, vals in per_dispatch(a.mfma_csv).values():
-        if vals.get("GRBM_GUI_ACTIVE", 0) > 0:
-            mf[name].append(vals.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (vals["GRBM_GUI_ACTIVE"] * a.simds))
+        mf[name].append(vals.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512 / a.peak_bf16 +
+                        vals.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0) * 512 / a.peak_f32)
     (fetch, fetch_id), (write, write_id) = read(a.fetch_csv, "FETCH_SIZE"), read(a.write_csv, "WRITE_SIZE")
     copy_bytes = a.copy_mib * (1 << 20)
     did, (_, cw) = max(((i, nv) for i, nv in write_id.items() if COPY in nv[0]), key=lambda t: t[1][1])
@@ -75,7 +78,7 @@ def main(argv=None):
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:a.top]:
         name, t, avg = r["Name"], float(r["TotalDurationNs"]), float(r["AverageNs"])
         u = mf.get(name)
-        util = sum(u) / len(u) if u else None
+        util = (sum(u) / len(u)) / (avg * 1e-9) if u and avg > 0 else None
         fb = [v for v in fetch.get(name, [])]
         wb = [v for v in write.get(name, [])]
         gbs = None
