@@ -103,7 +103,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Per key tile: K and V rows (next tile prefetched into registers).
 // ------------------------------------------------------------------------
 template <typename T, int HD>
-__global__ void __launch_bounds__(NW * 64, 4) attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ out,
+__global__ void __launch_bounds__(NW * 64, 3) attn_fwd_kernel(const T* __restrict__ qkv, T* __restrict__ out,
                                                               float* __restrict__ lse, int T_, int NH, float sl2) {
   typedef RowTile<T, HD> RT;
   constexpr int LD = RT::LD, ND = HD / 16, NDT = HD / 32;
@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(NW * 64, 4) attn_fwd_kernel(const T* __restric
   __shared__ __attribute__((aligned(16))) T Ks[2][KT * LD];
   __shared__ __attribute__((aligned(16))) T Vs[2][KT * LD];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), lr = lane & 31, lg = lane >> 5;
   const int qblk = gridDim.x - 1 - blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int C = NH * HD, S3 = 3 * C;
@@ -230,7 +230,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
   __shared__ __attribute__((aligned(16))) T Ks[2][KT * LD];
   __shared__ __attribute__((aligned(16))) T Vs[2][KT * LD];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), lr = lane & 31, lg = lane >> 5;
   const int qblk = gridDim.x - 1 - blockIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int C = NH * HD, S3 = 3 * C;
@@ -346,7 +346,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
   __shared__ __attribute__((aligned(16))) T Ds[2][KT * LD];
   __shared__ float Ls[2][KT], Dd[2][KT];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lr = lane & 31, lg = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), lr = lane & 31, lg = lane >> 5;
   const int kblk = blockIdx.x;  // early key blocks see the most queries: they go first
   const int h = blockIdx.y, b = blockIdx.z;
   const int C = NH * HD, S3 = 3 * C;

@@ -51,6 +51,11 @@ __device__ __forceinline__ void mma16(f32x16& acc, f32x8 a, f32x8 b) {
 template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return (T)x; }
 
+// Index of the calling wave in its block, known to the compiler to be the same
+// for every lane of the wave: branches on it (and on values derived from it)
+// become scalar branches instead of masked execution of both sides.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

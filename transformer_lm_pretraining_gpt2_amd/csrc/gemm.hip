@@ -150,7 +150,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   T (*sA)[OA::ELEMS] = reinterpret_cast<T (*)[OA::ELEMS]>(smem);
   T (*sB)[OB::ELEMS] = reinterpret_cast<T (*)[OB::ELEMS]>(smem + 2 * OA::ELEMS * sizeof(T));
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wi = wave / WJ, wj = wave % WJ;
   const int nbi = (g.M + BM - 1) / BM, nbj = (g.N + BN - 1) / BN;
   const int tile = xcd_remap(blockIdx.x, nbi * nbj);
