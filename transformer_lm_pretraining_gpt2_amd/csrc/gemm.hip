@@ -81,6 +81,17 @@ struct Operand {
       *reinterpret_cast<f32x4*>(s + gr * LD + gc * VE) = reg[c];
     }
   }
+  // part p of NP of the store (chunks spread over the substeps of a tile)
+  template <int NP>
+  __device__ __forceinline__ void store_part(T* s, int tid, int p) const {
+#pragma unroll
+    for (int c = 0; c < PER; c++) {
+      if (c * NP / PER != p) continue;
+      const int idx = tid + c * NT;
+      const int gr = idx / CPR, gc = idx % CPR;
+      *reinterpret_cast<f32x4*>(s + gr * LD + gc * VE) = reg[c];
+    }
+  }
   // Fragment of substep ks for rows rb .. rb+31: lane l gets row rb + l%32 and
   // reduction values 16*ks + 8*(l/32) + 0..7.
   static __device__ __forceinline__ F frag(const T* s, int rb, int ks, int lane) {
@@ -183,15 +194,23 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   // sum_r A(i, r) from the A fragments: each lane adds its 8 reduction values
   // per fragment in a fixed order.
   constexpr bool PIPE = AT == 0;
+  // With BK = 64 (four substeps per tile) the next tile's LDS stores are
+  // spread over the substeps, overlapping them with the MFMAs (they fill the
+  // other buffer, which the barrier after the tile protects); with two
+  // substeps the spread costs more than it hides.
+  constexpr bool ILV = BK / 16 >= 4;
   constexpr bool HAS_CS = gemm_has_colsum(AT, EPI, WI * WJ);
 #define GEMM_FRAGS(AS, BS, KS, FA, FB)                                                            \
   _Pragma("unroll") for (int ti = 0; ti < TI; ti++) FA[ti] = OA::frag(AS, wi * WTI + ti * 32, KS, lane); \
   _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) FB[tj] = OB::frag(BS, wj * WTJ + tj * 32, KS, lane);
-#define GEMM_COMPUTE(AS, BS, CSV, PP)                                                             \
+#define GEMM_COMPUTE(AS, BS, CSV, PP) GEMM_COMPUTE_ST(AS, BS, CSV, PP, (void)0)
+  // ST(ks): work interleaved with substep ks (the next tile's LDS stores)
+#define GEMM_COMPUTE_ST(AS, BS, CSV, PP, ST)                                                      \
   {                                                                                               \
     F fa[2][TI], fb[2][TJ];                                                                       \
     if constexpr (PP) { GEMM_FRAGS(AS, BS, 0, fa[0], fb[0]) }                                     \
     _Pragma("unroll") for (int ks = 0; ks < BK / 16; ks++) {                                      \
+      ST;                                                                                         \
       const int cur = PP ? ks & 1 : 0;                                                            \
       if constexpr (PP) {                                                                         \
         if (ks + 1 < BK / 16) { GEMM_FRAGS(AS, BS, ks + 1, fa[cur ^ 1], fb[cur ^ 1]) }            \
@@ -233,16 +252,28 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
       const int k2 = min(kbeg + (kt + 2) * BK, klast), k3 = min(kbeg + (kt + 3) * BK, klast);     \
       a0.load(k2);                                                                                \
       b0.load(k2);                                                                                \
-      GEMM_COMPUTE(sA[0], sB[0], CSV, PIPE)                                                       \
-      a1.store(sA[1], tid);                                                                       \
-      b1.store(sB[1], tid);                                                                       \
+      if constexpr (ILV) {                                                                        \
+        GEMM_COMPUTE_ST(sA[0], sB[0], CSV, PIPE,                                                  \
+                        (a1.template store_part<BK / 16>(sA[1], tid, ks),                         \
+                         b1.template store_part<BK / 16>(sB[1], tid, ks)))                        \
+      } else {                                                                                    \
+        GEMM_COMPUTE(sA[0], sB[0], CSV, PIPE)                                                     \
+        a1.store(sA[1], tid);                                                                     \
+        b1.store(sB[1], tid);                                                                     \
+      }                                                                                           \
       __syncthreads();                                                                            \
       /* buffer 1 holds tile kt+1, registers 0 hold tile kt+2 */                                  \
       a1.load(k3);                                                                                \
       b1.load(k3);                                                                                \
-      GEMM_COMPUTE(sA[1], sB[1], CSV, PIPE)                                                       \
-      a0.store(sA[0], tid);                                                                       \
-      b0.store(sB[0], tid);                                                                       \
+      if constexpr (ILV) {                                                                        \
+        GEMM_COMPUTE_ST(sA[1], sB[1], CSV, PIPE,                                                  \
+                        (a0.template store_part<BK / 16>(sA[0], tid, ks),                         \
+                         b0.template store_part<BK / 16>(sB[0], tid, ks)))                        \
+      } else {                                                                                    \
+        GEMM_COMPUTE(sA[1], sB[1], CSV, PIPE)                                                     \
+        a0.store(sA[0], tid);                                                                     \
+        b0.store(sB[0], tid);                                                                     \
+      }                                                                                           \
       __syncthreads();                                                                            \
     }                                                                                             \
     if (nk & 1) { /* the last tile sits in buffer 0 (no read-ahead: registers are tight here) */  \
@@ -266,6 +297,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
 
 #undef GEMM_MAINLOOP
 #undef GEMM_COMPUTE
+#undef GEMM_COMPUTE_ST
 #undef GEMM_FRAGS
   if (do_cs && wj == 0) {
 #pragma unroll
@@ -365,11 +397,10 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
 //    products and short reductions.  With BK = 32 (41 KB of LDS, three
 //    blocks per CU) it is the weight-gradient tile.
 //  * 8 waves, 256x256 (waves of 128x64, two per SIMD, twice the operand
-//    reuse): large outputs with short reductions (MLP up-projection, tied
-//    head forward and weight gradient).
-//  * 4 waves, 256x192, BK = 32: long reductions with a 768-wide output
-//    (MLP down-projection, input gradients of fc/qkv/tied head) and the
-//    smallest weight gradient.
+//    reuse): forward and input-gradient products with large outputs or long
+//    reductions (MLP up- and down-projection, tied head, input gradients of
+//    fc, qkv and the tied head); with BK = 32 the tied head's weight gradient.
+//  * 4 waves, 256x192, BK = 32: the smallest weight gradient.
 enum TileKind { TILE_128 = 0, TILE_128_K32, TILE_256x192_K32, TILE_256_W8, TILE_256_W8_K32 };
 
 TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
@@ -380,7 +411,6 @@ TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
     if (mn <= 1000000 && N % 192 == 0) return TILE_256x192_K32;
     return TILE_128_K32;
   }
-  if (K >= 2048 && N % 192 == 0) return TILE_256x192_K32;
   if (K >= 2048 || mn >= 40000000) return TILE_256_W8;
   return TILE_128;
 }
@@ -394,8 +424,8 @@ template <typename T, int AT, int BT, int EPI>
 hipError_t launch_tiled(hipStream_t st, const GemmArgs& g, TileKind k) {
   if constexpr (sizeof(T) == 2) {
     if (k == TILE_256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI, 64>(st, g);
-    if (k == TILE_256x192_K32) return launch<T, 256, 192, 2, 2, AT, BT, EPI, 32>(st, g);
     if constexpr (AT == 1) {
+      if (k == TILE_256x192_K32) return launch<T, 256, 192, 2, 2, AT, BT, EPI, 32>(st, g);
       if (k == TILE_256_W8_K32) return launch<T, 256, 256, 2, 4, AT, BT, EPI, 32>(st, g);
       if (k == TILE_128_K32) return launch<T, 128, 128, 2, 2, AT, BT, EPI, 32>(st, g);
     }
