@@ -23,43 +23,49 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 // LayerNorm forward: one wave per row; mean and biased variance over C,
 // y = (x - mean) * rstd * g + b, rstd = 1/sqrt(var + 1e-5).
-// Lane l holds elements 2l + 128k, 2l + 128k + 1 (k < NP = C/128).
+// Lane l holds elements VE*l + 64*VE*k .. +VE-1 (k < C / (64*VE)): 16-byte
+// loads (VE = 4) when C is a multiple of 256, else VE = 2.
 // ---------------------------------------------------------------------------
 template <typename T, int NP>
 __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ g,
                                                      const float* __restrict__ b, T* __restrict__ y,
                                                      float* __restrict__ mean, float* __restrict__ rstd, int M) {
-  typedef typename Pair<T>::type P;
   constexpr int C = NP * 128;
+  constexpr int VE = C % 256 == 0 ? 4 : 2, NC = C / (64 * VE);
+  typedef float fv __attribute__((ext_vector_type(VE)));
+  typedef T tv __attribute__((ext_vector_type(VE)));
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;
   const float* xr = x + (int64_t)row * C;
-  f32x2 v[NP];
+  fv v[NC];
   float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < NP; k++) {
-    v[k] = *reinterpret_cast<const f32x2*>(xr + 2 * lane + 128 * k);
-    s += v[k][0] + v[k][1];
+  for (int k = 0; k < NC; k++) {
+    v[k] = *reinterpret_cast<const fv*>(xr + VE * lane + 64 * VE * k);
+#pragma unroll
+    for (int e = 0; e < VE; e++) s += v[k][e];
   }
   const float mu = wave_sum(s) * (1.f / C);
   float q = 0.f;
 #pragma unroll
-  for (int k = 0; k < NP; k++) {
-    const float a = v[k][0] - mu, c = v[k][1] - mu;
-    q += a * a + c * c;
-  }
+  for (int k = 0; k < NC; k++)
+#pragma unroll
+    for (int e = 0; e < VE; e++) {
+      const float a = v[k][e] - mu;
+      q += a * a;
+    }
   const float rs = 1.f / sqrtf(wave_sum(q) * (1.f / C) + 1e-5f);
   T* yr = y + (int64_t)row * C;
 #pragma unroll
-  for (int k = 0; k < NP; k++) {
-    const int c0 = 2 * lane + 128 * k;
-    const f32x2 gg = *reinterpret_cast<const f32x2*>(g + c0);
-    const f32x2 bb = *reinterpret_cast<const f32x2*>(b + c0);
-    P o;
-    o[0] = from_f<T>((v[k][0] - mu) * rs * gg[0] + bb[0]);
-    o[1] = from_f<T>((v[k][1] - mu) * rs * gg[1] + bb[1]);
-    *reinterpret_cast<P*>(yr + c0) = o;
+  for (int k = 0; k < NC; k++) {
+    const int c0 = VE * lane + 64 * VE * k;
+    const fv gg = *reinterpret_cast<const fv*>(g + c0);
+    const fv bb = *reinterpret_cast<const fv*>(b + c0);
+    tv o;
+#pragma unroll
+    for (int e = 0; e < VE; e++) o[e] = from_f<T>((v[k][e] - mu) * rs * gg[e] + bb[e]);
+    *reinterpret_cast<tv*>(yr + c0) = o;
   }
   if (lane == 0) {
     mean[row] = mu;
