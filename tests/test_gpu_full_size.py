@@ -107,3 +107,18 @@ def test_small_config_launch_shape():
     # small GPT (V 4096, L 4, nh 4, C 256) at its own B = 64, T = 256
     rc = CONFIGS["small"]
     _repeated_step(rc.model, rc.B, rc.T, "bf16", seed=64)
+
+
+def test_full_size_fp32_step():
+    # fp32 mode at the 124M launch shape: operands beyond 2 GiB (the fp32
+    # logits are 3.3 GB) against the oracle in fp64, at the fp32 tolerances
+    p0 = synth.init_params(binding.param_layout(MODEL), MODEL.n_layer, MODEL.vocab_size)
+    ids, tgt = batches(MODEL, 1, T, 1, seed=99)[0]
+    rep = (np.repeat(ids, B, axis=0), np.repeat(tgt, B, axis=0))
+    print("gpu step (B=16, T=1024, fp32)", flush=True)
+    g = gpu_step(MODEL, B, T, "fp32", p0, [rep])
+    print("oracle step (B=1, fp64)", flush=True)
+    o = oracle_step(MODEL, p0, [(ids, tgt)], R=np.float64)
+    g["rows"] = [g["rows"][0][k * T:(k + 1) * T] for k in range(B)]
+    o["rows"] = [o["rows"][0]] * B
+    compare(MODEL, g, o, "fp32")

@@ -43,16 +43,18 @@ struct Operand {
   typedef typename Frag<T>::type F;
   f32x4 reg[PER];
   // Global loads go through a buffer descriptor (base address in scalar
-  // registers): each chunk keeps one loop-invariant 32-bit byte offset and the
-  // reduction step is a uniform scalar offset.  The host checks that every
-  // operand spans less than 4 GiB.
-  __amdgpu_buffer_rsrc_t rsrc;
+  // registers) whose base sits at the block's first row (reduction-contiguous
+  // operands) or at the current reduction step (strided operands), so each
+  // chunk's 32-bit byte offset stays inside one tile however large the
+  // operand is; it is loop-invariant, and the reduction step is a uniform
+  // scalar offset (contiguous operands) or a new base (strided operands).
+  const T* base;
+  int64_t ld_;
   uint32_t voff[PER];
-  int64_t kstride;  // bytes per reduction index
 
   __device__ __forceinline__ void init(const T* X, int64_t ld, int row0, int nrows, int tid) {
-    rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(X), 0, -1, 0x00020000);
-    kstride = TRANS ? ld * (int64_t)sizeof(T) : (int64_t)sizeof(T);
+    ld_ = ld;
+    base = TRANS ? X : X + (int64_t)row0 * ld;  // row0 < nrows: every tile starts inside the operand
 #pragma unroll
     for (int c = 0; c < PER; c++) {
       const int idx = tid + c * NT;
@@ -60,7 +62,7 @@ struct Operand {
       if constexpr (TRANS == 0) {
         // rows past the edge re-read the last row: they only feed outputs the epilogue drops
         const int r = min(row0 + gr, nrows - 1);
-        voff[c] = (uint32_t)(((int64_t)r * ld + gc * VE) * (int64_t)sizeof(T));
+        voff[c] = (uint32_t)(((int64_t)(r - row0) * ld + gc * VE) * (int64_t)sizeof(T));
       } else {
         const int col = min(row0 + gc * VE, nrows - VE);
         voff[c] = (uint32_t)(((int64_t)gr * ld + col) * (int64_t)sizeof(T));
@@ -68,7 +70,14 @@ struct Operand {
     }
   }
   __device__ __forceinline__ void load(int k0) {
-    const int soff = (int)(k0 * kstride);
+    __amdgpu_buffer_rsrc_t rsrc;
+    int soff = 0;
+    if constexpr (TRANS == 0) {
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), 0, -1, 0x00020000);
+      soff = k0 * (int)sizeof(T);
+    } else {
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base + (int64_t)k0 * ld_), 0, -1, 0x00020000);
+    }
 #pragma unroll
     for (int c = 0; c < PER; c++)
       reg[c] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff[c], soff, 0));
