@@ -48,6 +48,11 @@ def test_workspace_and_shape_checks():
     assert binding.check_shapes(m, 16, 1000) == -2  # T % 64
     assert binding.check_shapes(m, 16, 2048) == -2  # T > max_seq_len
     assert binding.check_shapes(m, 1, 64) == -2  # B*T % 128
+    assert binding.check_shapes(m, 0, 1024) == -2  # empty batch
+    assert binding.check_shapes(m, 16, 0) == -2  # empty sequences
+    assert binding.check_shapes(m, -16, 1024) == -2
+    assert binding.check_shapes(m, 1 << 17, 1024) == -2  # B*T beyond 2^26 tokens
+    assert binding.check_shapes(m, 1, 128) == 0  # one sequence filling one 128-row tile
     bad = [GPT2Config(50257, 50257, 12, 12, 768, 1024),  # Vp % 128
            GPT2Config(50257, 50176, 12, 12, 768, 1024),  # Vp < V
            GPT2Config(512, 512, 2, 3, 128, 64),  # C % nh

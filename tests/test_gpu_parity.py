@@ -124,3 +124,36 @@ def test_nonfinite_gradient_skips_the_update():
     assert s.sync_status() == -6
     assert np.array_equal(s.params.cpu().numpy(), p0)
     assert s.sync_status() == 0
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_single_sequence_one_tile(prec):
+    # B = 1, T = 128: every matmul is a single 128-row tile, attention two key tiles
+    m = GPT2Config(vocab_size=509, padded_vocab_size=512, n_layer=2, n_head=4, n_embd=128, max_seq_len=128)
+    p0 = synth.random_params(binding.param_layout(m), m.vocab_size, seed=11, scale=0.05)
+    mb = batches(m, 1, 128, 1, seed=12)
+    g = gpu_step(m, 1, 128, prec, p0, mb)
+    o = oracle_step(m, p0, mb)
+    compare(m, g, o, prec)
+
+
+def test_one_layer_heavy_vocab_padding():
+    # one block; V = 130 padded to 256 (most of the last vocabulary tile is padding)
+    m = GPT2Config(vocab_size=130, padded_vocab_size=256, n_layer=1, n_head=2, n_embd=128, max_seq_len=128)
+    p0 = synth.random_params(binding.param_layout(m), m.vocab_size, seed=13, scale=0.05)
+    mb = batches(m, 2, 64, 1, seed=14, data="uniform")
+    g = gpu_step(m, 2, 64, "fp32", p0, mb)
+    o = oracle_step(m, p0, mb)
+    compare(m, g, o, "fp32")
+
+
+def test_all_positions_same_token():
+    # every input position holds the last real id: the embedding scatter sums
+    # one segment of all B*T positions (four 64-position pieces)
+    lay = binding.param_layout(PADDED)
+    p0 = synth.random_params(lay, PADDED.vocab_size, seed=15, scale=0.05)
+    ids = np.full((2, 128), PADDED.vocab_size - 1, np.int32)
+    tgt = np.random.default_rng(16).integers(0, PADDED.vocab_size, (2, 128)).astype(np.int32)
+    g = gpu_step(PADDED, 2, 128, "fp32", p0, [(ids, tgt)])
+    o = oracle_step(PADDED, p0, [(ids, tgt)])
+    compare(PADDED, g, o, "fp32")
