@@ -157,3 +157,18 @@ def test_all_positions_same_token():
     g = gpu_step(PADDED, 2, 128, "fp32", p0, [(ids, tgt)])
     o = oracle_step(PADDED, p0, [(ids, tgt)])
     compare(PADDED, g, o, "fp32")
+
+
+def test_overlapped_weight_gradients_match_serial():
+    # the second stream only changes when the weight-gradient products run,
+    # never what they compute: both schedules give bit-identical results
+    lay = binding.param_layout(SMALL)
+    p0 = synth.init_params(lay, SMALL.n_layer, SMALL.vocab_size, dtype=np.float64)
+    mb = batches(SMALL, 4, 256, 2, seed=31)
+    a = gpu_step(SMALL, 4, 256, "bf16", p0, mb)
+    s = binding.TrainStep(SMALL, 4, 256, "bf16")
+    s.set_overlap(False)
+    b = gpu_step(SMALL, 4, 256, "bf16", p0, mb, handle=s)
+    assert a["loss"] == b["loss"]
+    for k in ("grads", "params", "m", "v"):
+        assert np.array_equal(a[k], b[k]), k

@@ -46,6 +46,7 @@ SIGNATURES = [
     ("gpt2_destroy", None, [_P]),
     ("gpt2_refresh_params", _I, [_P]),
     ("gpt2_set_stream", _I, [_P, _P]),
+    ("gpt2_set_overlap", _I, [_P, _I]),
     ("gpt2_forward", _I, [_P, _P, _P, _P, _P]),
     ("gpt2_backward", _I, [_P, _I, _I]),
     ("gpt2_adamw_step", _I, [_P, _I, _F, _F, _F, _F, _F, _F, _P]),
@@ -191,6 +192,10 @@ class TrainStep:
     def sync_status(self):
         """Returns the deferred status code (0 = ok) after synchronising."""
         return int(lib().gpt2_sync_status(self.h))
+
+    def set_overlap(self, enable=True):
+        """Weight-gradient products on the handle's second stream (default) or all on one stream."""
+        self._check(lib().gpt2_set_overlap(self.h, 1 if enable else 0), "set_overlap")
 
     def timing_enable(self, kernel_name, enable=True):
         kid = kernel_names().index(kernel_name)

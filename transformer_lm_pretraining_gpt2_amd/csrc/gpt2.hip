@@ -197,6 +197,13 @@ struct gpt2_handle {
   void* params_lp;
   char* ws;
   hipStream_t st;
+  // The per-layer weight-gradient products run on a second stream owned by
+  // the library, overlapping the rest of the layer's backward; events order
+  // them after their inputs and before anything that overwrites those inputs
+  // or reads their partial sums.
+  hipStream_t side = nullptr;
+  bool overlap = true;
+  hipEvent_t ev_fork = nullptr, ev_done[4] = {nullptr, nullptr, nullptr, nullptr};
   Layout lay;
   Plan plan;
   std::vector<const Tensor*> by_kind_layer;  // [kind * (L+1) + layer+1]
@@ -380,6 +387,28 @@ int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* d
   return rc;
 }
 
+// A weight-gradient product on the side stream: it starts after everything
+// enqueued so far on the main stream and signals ev_done[wkind] when done.
+int side_weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* dW, float* db, int wkind,
+                     int accumulate, const char* what) {
+  if (!h->overlap) return weight_grad(h, dY, X, N, K, dW, db, wkind, accumulate, what);
+  int rc = hip_check(h, hipEventRecord(h->ev_fork, h->st), "fork");
+  if (!rc) rc = hip_check(h, hipStreamWaitEvent(h->side, h->ev_fork, 0), "fork wait");
+  if (rc) return rc;
+  hipStream_t main = h->st;
+  h->st = h->side;
+  rc = weight_grad(h, dY, X, N, K, dW, db, wkind, accumulate, what);
+  h->st = main;
+  if (!rc) rc = hip_check(h, hipEventRecord(h->ev_done[wkind], h->side), "join");
+  return rc;
+}
+
+// The main stream waits for the side-stream product of weight kind wkind.
+int join_weight_grad(gpt2_t* h, int wkind) {
+  if (!h->overlap) return GPT2_OK;
+  return hip_check(h, hipStreamWaitEvent(h->st, h->ev_done[wkind], 0), "join wait");
+}
+
 int ln_backward(gpt2_t* h, const void* dy, const float* x, const float* mean, const float* rstd, int kind_g, int layer,
                 int slot, int accumulate_dres, int accumulate_grads) {
   const int C = h->cfg.n_embd, M = (int)h->M;
@@ -478,6 +507,16 @@ int gpt2_init(gpt2_t** out, const gpt2_config_t* cfg, int precision, int B, int 
     delete h;
     return GPT2_ERR_HIP;
   }
+  if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess) {
+    gpt2_destroy(h);
+    return GPT2_ERR_HIP;
+  }
+  for (auto& e : h->ev_done)
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+      gpt2_destroy(h);
+      return GPT2_ERR_HIP;
+    }
   *out = h;
   return GPT2_OK;
 }
@@ -488,12 +527,25 @@ void gpt2_destroy(gpt2_t* h) {
     (void)hipEventDestroy(t.a);
     (void)hipEventDestroy(t.b);
   }
+  if (h->side) {
+    (void)hipStreamSynchronize(h->side);
+    (void)hipStreamDestroy(h->side);
+  }
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  for (auto& e : h->ev_done)
+    if (e) (void)hipEventDestroy(e);
   delete h;
 }
 
 int gpt2_set_stream(gpt2_t* h, void* stream) {
   if (!h) return GPT2_ERR_ARG;
   h->st = static_cast<hipStream_t>(stream);
+  return GPT2_OK;
+}
+
+int gpt2_set_overlap(gpt2_t* h, int enable) {
+  if (!h) return GPT2_ERR_ARG;
+  h->overlap = enable != 0;
   return GPT2_OK;
 }
 
@@ -632,25 +684,27 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
 
   for (int l = L - 1; l >= 0; l--) {
     // MLP down-projection: dres is the gradient of the block output
-    if ((rc = weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), 3,
-                          acc, "fcproj dw")))
+    if ((rc = side_weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), 3,
+                               acc, "fcproj dw")))
       return rc;
     g = dx_args(h, dres_op, h->W(T_FCPW, l), C, 4 * C, h->w<void>(P.du));
     g.aux = h->w<void>(P.u[l]);
     g.ldaux = 4 * C;
     if ((rc = run_gemm(h, K_GEMM_NN_GELU_BWD, 0, 1, EPI_GELU_BWD, g, "fcproj dx"))) return rc;
     // MLP up-projection
-    if ((rc = weight_grad(h, h->w<void>(P.du), h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), h->G32(T_FCB, l),
-                          2, acc, "fc dw")))
+    if ((rc = side_weight_grad(h, h->w<void>(P.du), h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), h->G32(T_FCB, l),
+                               2, acc, "fc dw")))
       return rc;
     g = dx_args(h, h->w<void>(P.du), h->W(T_FCW, l), 4 * C, C, h->w<void>(P.dh));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "fc dx"))) return rc;
+    // LayerNorm 2 rewrites the matmul copy of dres that the fcproj weight gradient reads
+    if ((rc = join_weight_grad(h, 3))) return rc;
     if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_mid[l]), h->w<float>(P.mean2[l]), h->w<float>(P.rstd2[l]),
                           T_LN2G, l, 1, 1, acc)))
       return rc;
     // attention output projection
-    if ((rc = weight_grad(h, dres_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l), 1,
-                          acc, "proj dw")))
+    if ((rc = side_weight_grad(h, dres_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l), 1,
+                               acc, "proj dw")))
       return rc;
     g = dx_args(h, dres_op, h->W(T_PROJW, l), C, C, h->w<void>(P.datty));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "proj dx"))) return rc;
@@ -675,14 +729,19 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
       if (rc) return rc;
     }
     // qkv projection
-    if ((rc = weight_grad(h, h->w<void>(P.dqkv), h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l), h->G32(T_QKVB, l),
-                          0, acc, "qkv dw")))
+    if ((rc = side_weight_grad(h, h->w<void>(P.dqkv), h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l),
+                               h->G32(T_QKVB, l), 0, acc, "qkv dw")))
       return rc;
     g = dx_args(h, h->w<void>(P.dqkv), h->W(T_QKVW, l), 3 * C, C, h->w<void>(P.dh));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "qkv dx"))) return rc;
+    // LayerNorm 1 rewrites the matmul copy of dres that the projection weight gradient reads
+    if ((rc = join_weight_grad(h, 1))) return rc;
     if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[l]), h->w<float>(P.mean1[l]), h->w<float>(P.rstd1[l]),
                           T_LN1G, l, 2, 1, acc)))
       return rc;
+    // the layer's partial sums are complete once the last side-stream product
+    // (qkv) is; the next layer overwrites du and dqkv only after this point
+    if ((rc = join_weight_grad(h, 0))) return rc;
     if ((rc = flush_reductions(h))) return rc;
   }
   if ((rc = flush_reductions(h))) return rc;
