@@ -145,13 +145,149 @@ __device__ __forceinline__ float frag_sum(f32x8 f, float acc) {
   return acc;
 }
 
+// Direct-to-LDS operand tile (bf16): buffer_load ... lds moves each lane's 16
+// bytes from global memory straight into LDS, with no staging registers.  One
+// such load writes 64 lanes x 16 bytes contiguously at a wave-uniform LDS
+// address, so the tile has no row padding; instead the 16-byte chunks of each
+// LDS row are permuted (XOR with a function of the row), which the loads apply
+// by choosing which global chunk each lane fetches and the fragment reads undo.
+//  TRANS = 0: LDS row q = operand row row0 + q, BK reduction values
+//  TRANS = 1: LDS row q = reduction index k0 + q, R operand rows (R = 128 or
+//             256, so every LDS row starts on the same bank)
+// The permutations keep each fragment read conflict-free for 32 or 64 banks:
+// the 16 (or 8) rows one pass of a 16-byte read touches land on distinct
+// 16-byte bank groups; the transposing reads spread their 8 rows over all
+// four 64-byte groups of a 256-byte bank line.
+template <int R, int BK, int NW, int TRANS>
+struct DtlOperand {
+  static constexpr int ROWB = TRANS ? R * 2 : BK * 2;  // bytes per LDS row
+  static constexpr int CPR = ROWB / 16;                // 16-byte chunks per LDS row
+  static constexpr int BYTES = R * BK * 2;
+  static constexpr int PER = BYTES / 1024 / NW;        // loads per wave per tile
+  static_assert(BYTES % (1024 * NW) == 0, "tile does not split evenly over the waves");
+  static_assert(TRANS ? (R == 128 || R == 256) : (CPR == 4 || CPR == 8), "unsupported tile for direct loads");
+  const bf16* base;
+  int64_t ld_;
+  uint32_t voff[PER];
+
+  // LDS position of logical chunk c in LDS row q (an involution: also the inverse)
+  static __device__ __forceinline__ int swz(int q, int c) {
+    if constexpr (TRANS) return c ^ ((q & 3) << 2);
+    else if constexpr (CPR == 8) return c ^ (((q >> 1) ^ ((q & 1) << 2)) & 7);
+    else return c ^ (((q >> 2) ^ (q & 2)) & 3);
+  }
+  __device__ __forceinline__ void init(const bf16* X, int64_t ld, int row0, int nrows, int wave, int lane) {
+    ld_ = ld;
+    base = TRANS ? X : X + (int64_t)row0 * ld;  // row0 < nrows: every tile starts inside the operand
+#pragma unroll
+    for (int c = 0; c < PER; c++) {
+      const int slot = (c * NW + wave) * 64 + lane;  // LDS chunk this lane fills
+      const int q = slot / CPR, lc = swz(q, slot % CPR);
+      if constexpr (TRANS == 0) {
+        // rows past the edge re-read the last row: they only feed outputs the epilogue drops
+        const int r = min(row0 + q, nrows - 1);
+        voff[c] = (uint32_t)(((int64_t)(r - row0) * ld + lc * 8) * 2);
+      } else {
+        const int col = min(row0 + lc * 8, nrows - 8);
+        voff[c] = (uint32_t)(((int64_t)q * ld + col) * 2);
+      }
+    }
+  }
+  // start the loads of the tile at reduction offset k0 into LDS at tile
+  __device__ __forceinline__ void issue(char* tile, int k0, int wave) const {
+    __amdgpu_buffer_rsrc_t rsrc;
+    int soff = 0;
+    if constexpr (TRANS == 0) {
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, -1, 0x00020000);
+      soff = k0 * 2;
+    } else {
+      rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base + (int64_t)k0 * ld_), 0, -1, 0x00020000);
+    }
+    // (device pass only: with the builtin in the host pass, clang omits the
+    // launch stubs of all but the first kernel instantiation using it)
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+    for (int c = 0; c < PER; c++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(tile + (c * NW + wave) * 1024),
+                                               16, voff[c], soff, 0, 0);
+#endif
+  }
+  // same fragment as Operand::frag (lane l: row rb + l%32, reduction values
+  // 16*ks + 8*(l/32) + 0..7)
+  static __device__ __forceinline__ bf16x8 frag(const char* tile, int rb, int ks, int lane) {
+    if constexpr (TRANS == 0) {
+      const int q = rb + (lane & 31);
+      return *reinterpret_cast<const bf16x8*>(tile + q * ROWB + swz(q, 2 * ks + (lane >> 5)) * 16);
+    } else {
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+      const int j = lane & 15;
+      const int kr = ks * 16 + 8 * (lane >> 5) + (j >> 2);
+      const int col = rb + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+      // rows kr and kr + 4 share the permutation
+      const char* p = tile + kr * ROWB + swz(kr, col >> 3) * 16 + (col & 7) * 2;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * ROWB));
+      const bf16x4 a = __builtin_bit_cast(bf16x4, lo), b = __builtin_bit_cast(bf16x4, hi);
+      return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+};
+
+// Wait until at most N of this wave's vector-memory loads are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
+}
+// Wait until the tiles issued after the one needed are the only ones in
+// flight: n tiles (of P loads each) were issued after it, at most MAX of them
+// may stay outstanding.  n is the same for the whole wave (scalar branches).
+template <int P, int MAX>
+__device__ __forceinline__ void wait_tiles_after(int n) {
+  if constexpr (MAX <= 0) {
+    wait_vm<0>();
+  } else {
+    if (n >= MAX) wait_vm<MAX * P>();
+    else wait_tiles_after<P, MAX - 1>(n);
+  }
+}
+// Workgroup barrier without the memory fence of __syncthreads (whose release
+// would wait for every load in flight, the next tiles' included); LDS
+// ordering is by the explicit waits around it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Instruction order of one substep (its MFMAs and the next fragments' LDS
+// reads): the reads go out two at a time between the first MFMAs, so their
+// latency hides behind the remaining MFMAs instead of stalling the next
+// substep (left alone, the scheduler sinks them to just before their use).
+template <int NM, int NR>
+__device__ __forceinline__ void dtl_schedule() {
+#pragma unroll
+  for (int r = 0; r < NR; r += 2) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR + 1) / 2, 0);  // the remaining MFMAs
+}
+
 // Which instantiations can produce the bias gradient: weight-gradient products
 // (strided A, fp32 output) on 4-wave tiles.  The 8-wave tile serves only the
 // bias-free tied output layer; a second copy of its main loop would not fit
 // its 256 registers.
 constexpr bool gemm_has_colsum(int at, int epi, int waves) { return at == 1 && epi == EPI_F32 && waves == 4; }
 
-template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI>
+// NBUF = 0: operands staged through registers (two register stages, two LDS
+// buffers).  NBUF >= 2 (bf16): direct-to-LDS loads into a ring of NBUF LDS
+// buffers, the tile NBUF steps ahead loading while the current one is used.
+template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI, int NBUF>
 __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   constexpr int NT = WI * WJ * 64;
   constexpr int WTI = BM / WI, WTJ = BN / WJ;
@@ -164,7 +300,10 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   // staging area for half of the output tile (fp32) share one LDS block.
   constexpr int RP = BM / WI;                 // output rows staged per pass (one row of waves)
   constexpr int SLD = BN + 4;                 // staging row length (floats)
-  constexpr int OPER_BYTES = 2 * (OA::ELEMS + OB::ELEMS) * (int)sizeof(T);
+  typedef DtlOperand<BM, BK, WI * WJ, AT> DA;
+  typedef DtlOperand<BN, BK, WI * WJ, BT> DB;
+  constexpr int DSTAGE = (BM + BN) * BK * 2;  // one ring buffer (both operands)
+  constexpr int OPER_BYTES = NBUF ? NBUF * DSTAGE : 2 * (OA::ELEMS + OB::ELEMS) * (int)sizeof(T);
   constexpr int STAGE_BYTES = RP * SLD * 4;
   __shared__ __attribute__((aligned(16))) char smem[OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES];
   T (*sA)[OA::ELEMS] = reinterpret_cast<T (*)[OA::ELEMS]>(smem);
@@ -290,6 +429,66 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
     }                                                                                             \
   }
 
+  // Direct-to-LDS main loop.  At the last substep of tile kt the wave waits
+  // for its own loads of tile kt+1 and for its reads of tile kt, then one
+  // barrier makes tile kt+1 visible and frees tile kt's buffer, which takes
+  // tile kt+NBUF; the first fragments of tile kt+1 are read while the last
+  // MFMAs of tile kt run.  Tiles past the last are never loaded (the waits
+  // count only the loads actually issued).
+#define GEMM_DFRAGS(TILE, KS, FA, FB)                                                                     \
+  _Pragma("unroll") for (int ti = 0; ti < TI; ti++) FA[ti] = DA::frag(TILE, wi * WTI + ti * 32, KS, lane); \
+  _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) FB[tj] = DB::frag(TILE + DA::BYTES, wj * WTJ + tj * 32, KS, lane);
+// One tile from LDS buffer CUR; unless LAST, its last substep also moves to
+// tile kt+1 (kept out of a runtime branch so the substep's MFMAs never wait
+// for the next tile's fragment reads)
+#define GEMM_DTL_TILE(CSV, LAST)                                                                          \
+  {                                                                                                       \
+    const char* cur = smem + (kt % NBUF) * DSTAGE;                                                        \
+    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ks++) {                                              \
+      const int c = ks & 1;                                                                               \
+      if (ks + 1 < BK / 16) {                                                                             \
+        GEMM_DFRAGS(cur, ks + 1, fa[c ^ 1], fb[c ^ 1])                                                    \
+      } else if constexpr (!LAST) {                                                                       \
+        wait_tiles_after<P, NBUF - 2>(nk - 2 - kt);                                                       \
+        lds_barrier();                                                                                    \
+        if (kt + NBUF < nk) {                                                                             \
+          da.issue(smem + (kt % NBUF) * DSTAGE, kbeg + (kt + NBUF) * BK, wave);                           \
+          db.issue(smem + (kt % NBUF) * DSTAGE + DA::BYTES, kbeg + (kt + NBUF) * BK, wave);               \
+        }                                                                                                 \
+        const char* nxt = smem + ((kt + 1) % NBUF) * DSTAGE;                                              \
+        GEMM_DFRAGS(nxt, 0, fa[c ^ 1], fb[c ^ 1])                                                         \
+      }                                                                                                   \
+      if constexpr (CSV) {                                                                                \
+        _Pragma("unroll") for (int ti = 0; ti < TI; ti++) cs[ti] = frag_sum(fa[c][ti], cs[ti]);           \
+      }                                                                                                   \
+      _Pragma("unroll") for (int ti = 0; ti < TI; ti++)                                                   \
+        _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) mma16(acc[ti][tj], fb[c][tj], fa[c][ti]);       \
+      if (ks + 1 < BK / 16 || !LAST) dtl_schedule<TI * TJ, NREAD>();                                      \
+    }                                                                                                     \
+  }
+#define GEMM_DTL_LOOP(CSV)                                                                                \
+  {                                                                                                       \
+    constexpr int P = DA::PER + DB::PER;                                                                  \
+    constexpr int NREAD = TI * (AT ? 2 : 1) + TJ * (BT ? 2 : 1);                                          \
+    DA da;                                                                                                \
+    DB db;                                                                                                \
+    da.init(static_cast<const bf16*>(g.A), g.lda, i0, g.M, wave, lane);                                   \
+    db.init(static_cast<const bf16*>(g.B), g.ldb, j0, g.N, wave, lane);                                   \
+    _Pragma("unroll") for (int s = 0; s < NBUF; s++) {                                                    \
+      if (s < nk) {                                                                                       \
+        da.issue(smem + s * DSTAGE, kbeg + s * BK, wave);                                                 \
+        db.issue(smem + s * DSTAGE + DA::BYTES, kbeg + s * BK, wave);                                     \
+      }                                                                                                   \
+    }                                                                                                     \
+    wait_tiles_after<P, NBUF - 1>(nk - 1);                                                                \
+    lds_barrier();                                                                                        \
+    bf16x8 fa[2][TI], fb[2][TJ];                                                                          \
+    GEMM_DFRAGS(smem, 0, fa[0], fb[0])                                                                    \
+    int kt = 0;                                                                                           \
+    _Pragma("unroll 1") for (; kt < nk - 1; kt++) GEMM_DTL_TILE(CSV, false)                               \
+    GEMM_DTL_TILE(CSV, true)                                                                              \
+  }
+
   // Only the blocks of the first column tile (bj == 0) sum the bias gradient
   // (and of those only the waves with wj == 0 write it).  The choice is made
   // once per block, outside the main loop, so the loop itself stays one
@@ -298,12 +497,22 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   float cs[TI];
 #pragma unroll
   for (int ti = 0; ti < TI; ti++) cs[ti] = 0.f;
-  if constexpr (HAS_CS) {
+  if constexpr (NBUF > 0) {
+    static_assert(sizeof(T) == 2 && BK % 32 == 0, "direct-to-LDS loads: bf16, even substep count");
+    if constexpr (HAS_CS) {
+      if (do_cs) GEMM_DTL_LOOP(1) else GEMM_DTL_LOOP(0)
+    } else {
+      GEMM_DTL_LOOP(0)
+    }
+  } else if constexpr (HAS_CS) {
     if (do_cs) GEMM_MAINLOOP(1) else GEMM_MAINLOOP(0)
   } else {
     GEMM_MAINLOOP(0)
   }
 
+#undef GEMM_DTL_LOOP
+#undef GEMM_DTL_TILE
+#undef GEMM_DFRAGS
 #undef GEMM_MAINLOOP
 #undef GEMM_COMPUTE
 #undef GEMM_COMPUTE_ST
@@ -385,7 +594,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   }
 }
 
-template <typename T, int BM, int BN, int WI, int WJ, int AT, int BT, int EPI, int BK>
+template <typename T, int BM, int BN, int WI, int WJ, int AT, int BT, int EPI, int BK, int NBUF = 0>
 hipError_t launch(hipStream_t st, const GemmArgs& g) {
   constexpr int VE = Vec16<T>::n;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
@@ -395,7 +604,7 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
     return hipErrorInvalidValue;
   const int nbi = (g.M + BM - 1) / BM, nbj = (g.N + BN - 1) / BN;
   dim3 grid(nbi * nbj, g.splits);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WI, WJ, AT, BT, EPI>), grid, dim3(WI * WJ * 64), 0, st, g);
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WI, WJ, AT, BT, EPI, NBUF>), grid, dim3(WI * WJ * 64), 0, st, g);
   return hipGetLastError();
 }
 
@@ -410,7 +619,17 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
 //    reductions (MLP up- and down-projection, tied head, input gradients of
 //    fc, qkv and the tied head); with BK = 32 the tied head's weight gradient.
 //  * 4 waves, 256x192, BK = 32: the smallest weight gradient.
-enum TileKind { TILE_128 = 0, TILE_128_K32, TILE_256x192_K32, TILE_256_W8, TILE_256_W8_K32 };
+//  * 8 waves, 256x192 (waves of 64x96), BK = 64: forward and input-gradient
+//    products whose output width is a multiple of 192 up to 2304 (the
+//    model-width outputs: 16384 x 768 makes 64 x 4 = 256 tiles, one per CU,
+//    where 256x256 leaves a quarter of the CUs idle; and the qkv projection).
+//  * The 8-wave 256x256 tile with direct-to-LDS operand loads (two LDS
+//    buffers, BK = 64): other forward products up to 4096 wide (both operands
+//    reduction-contiguous), where it saves the staging registers.  Its single
+//    tile of look-ahead is too short for the tied head's long sweep.
+enum TileKind {
+  TILE_128 = 0, TILE_128_K32, TILE_256x192_K32, TILE_256_W8, TILE_256_W8_K32, TILE_D256_W8, TILE_192_W8
+};
 
 TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
   if (p != BF16 || M < 256) return TILE_128;
@@ -420,18 +639,25 @@ TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
     if (mn <= 1000000 && N % 192 == 0) return TILE_256x192_K32;
     return TILE_128_K32;
   }
-  if (K >= 2048 || mn >= 40000000) return TILE_256_W8;
+  if (N % 192 == 0 && N <= 2304 && mn >= 4000000) return TILE_192_W8;
+  if (K >= 2048 || mn >= 40000000) return (!a_t && !b_t && N <= 4096) ? TILE_D256_W8 : TILE_256_W8;
   return TILE_128;
 }
 
 int tile_bk(Prec p, TileKind k) {
   if (p != BF16) return 32;
-  return (k == TILE_128 || k == TILE_256_W8) ? 64 : 32;
+  return (k == TILE_128 || k == TILE_256_W8 || k == TILE_D256_W8 || k == TILE_192_W8) ? 64 : 32;
 }
 
 template <typename T, int AT, int BT, int EPI>
 hipError_t launch_tiled(hipStream_t st, const GemmArgs& g, TileKind k) {
   if constexpr (sizeof(T) == 2) {
+    if constexpr (AT == 0 && BT == 0) {
+      if (k == TILE_D256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI, 64, 2>(st, g);
+    }
+    if constexpr (AT == 0) {
+      if (k == TILE_192_W8) return launch<T, 256, 192, 4, 2, AT, BT, EPI, 64>(st, g);
+    }
     if (k == TILE_256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI, 64>(st, g);
     if constexpr (AT == 1) {
       if (k == TILE_256x192_K32) return launch<T, 256, 192, 2, 2, AT, BT, EPI, 32>(st, g);
@@ -471,7 +697,8 @@ hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArg
 int gemm_split_hint(Prec p, int a_t, int b_t, int M, int N, int K) {
   const TileKind k = choose_tile(p, a_t, b_t, M, N, K);
   const int bm = (k == TILE_128 || k == TILE_128_K32) ? 128 : 256;
-  const int bn = k == TILE_256x192_K32 ? 192 : (k == TILE_256_W8 || k == TILE_256_W8_K32) ? 256 : 128;
+  const int bn = (k == TILE_256x192_K32 || k == TILE_192_W8) ? 192
+                 : (k == TILE_256_W8 || k == TILE_256_W8_K32 || k == TILE_D256_W8) ? 256 : 128;
   const int bk = tile_bk(p, k);
   const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   // one block per CU for the large tiles, two for 128x128; the reduction must
