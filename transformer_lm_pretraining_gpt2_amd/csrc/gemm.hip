@@ -532,6 +532,31 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   // j = tile col base + 8*(r/4) + 4*(l/32) + r%4.
   float* stage = reinterpret_cast<float*>(smem);
   constexpr int CPRW = BN / 8;  // 8-column chunks per staged row
+  // Each thread takes NCH 8-column chunks of the staged rows per pass.  Their
+  // columns are the same in every pass, so the bias is loaded once, before
+  // the passes; the inputs that depend on the row (residual, gelu', the
+  // accumulated partial) are loaded a batch at a time, every load of a batch
+  // issued before its first store, so a batch pays one memory latency rather
+  // than one per chunk (the stores might alias the inputs, so the compiler
+  // would not hoist the loads above them by itself).
+  constexpr int NCH = (RP * CPRW + NT - 1) / NT;
+  constexpr bool HAS_BIAS = EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID;
+  constexpr int NBV = HAS_BIAS ? (NT % CPRW == 0 ? 1 : NCH) : 1;  // distinct bias chunks per thread
+  static_assert(NBV <= 4, "bias chunks per thread");
+  // (batches measured: one chunk at a time is as fast or faster for gelu',
+  // the plain store and the fp32 partials, whose 8-wave kernels spill)
+  // (and a thread with several bias chunks takes all its chunks at once, so
+  // the bias array is indexed with constants)
+  constexpr int BATCH = EPI == EPI_RESID ? (NCH < 3 ? NCH : 3) : NBV > 1 ? NCH : 1;
+  static_assert(NBV == 1 || BATCH % NBV == 0 || BATCH == NCH, "bias chunk index must be a constant");
+  const bool use_bias = HAS_BIAS && (EPI != EPI_STORE || g.bias != nullptr);
+  f32x8 bv[NBV];
+#pragma unroll
+  for (int k = 0; k < NBV; k++) {
+    const int j = j0 + ((tid + k * NT) % CPRW) * 8;
+    bv[k] = f32x8{};
+    if (use_bias && j < g.N) bv[k] = ld8(g.bias + j);
+  }
 #pragma unroll 1
   for (int pass = 0; pass < WI; pass++) {
     __syncthreads();  // operand tiles (or the previous pass) are no longer read
@@ -548,48 +573,75 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
           }
     }
     __syncthreads();
-    for (int c = tid; c < RP * CPRW; c += NT) {
-      const int il = c / CPRW, jl = (c % CPRW) * 8;
-      const int i = i0 + pass * RP + il, j = j0 + jl;
-      if (i >= g.M || j >= g.N) continue;
-      const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl);
-      const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl + 4);
-      f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      if constexpr (EPI == EPI_STORE || EPI == EPI_F32) v *= g.alpha;
-      if constexpr (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID) {
-        if (EPI != EPI_STORE || g.bias) v += ld8(g.bias + j);
-      }
-      if constexpr (EPI == EPI_STORE) {
-        F o;
+    auto chunk_batch = [&](const int b0) {
+      f32x8 x[BATCH];
+      F u[BATCH];
 #pragma unroll
-        for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e]);
-        st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
-      } else if constexpr (EPI == EPI_GELU) {
-        // the backward needs only gelu' at the pre-activation: store that
-        // (from the fp32 value) next to the activation
-        F u, o;
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const float sg = gelu_sigmoid(v[e]);
-          u[e] = from_f<T>(gelu_tanh_grad_s(v[e], sg));
-          o[e] = from_f<T>(v[e] * sg);
+      for (int k = 0; k < BATCH; k++) {
+        const int c = tid + (b0 + k) * NT;
+        const int il = c / CPRW, jl = (c % CPRW) * 8;
+        const int i = i0 + pass * RP + il, j = j0 + jl;
+        if (b0 + k < NCH && c < RP * CPRW && i < g.M && j < g.N) {
+          if constexpr (EPI == EPI_RESID) x[k] = ld8(g.resid + (int64_t)i * g.ldr + j);
+          if constexpr (EPI == EPI_GELU_BWD) u[k] = ld8(static_cast<const T*>(g.aux) + (int64_t)i * g.ldaux + j);
+          if constexpr (EPI == EPI_F32) {
+            if (g.accumulate)
+              x[k] = ld8(static_cast<const float*>(g.C) + (int64_t)blockIdx.y * g.split_stride + (int64_t)i * g.ldc + j);
+          }
         }
-        st8(static_cast<T*>(g.aux) + (int64_t)i * g.ldaux + j, u);
-        st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
-      } else if constexpr (EPI == EPI_RESID) {
-        v += ld8(g.resid + (int64_t)i * g.ldr + j);
-        st8(static_cast<float*>(g.C) + (int64_t)i * g.ldc + j, v);
-      } else if constexpr (EPI == EPI_GELU_BWD) {
-        const F u = ld8(static_cast<const T*>(g.aux) + (int64_t)i * g.ldaux + j);
-        F o;
-#pragma unroll
-        for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e] * to_f<T>(u[e]));
-        st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
-      } else {  // EPI_F32
-        float* Cp = static_cast<float*>(g.C) + (int64_t)blockIdx.y * g.split_stride + (int64_t)i * g.ldc + j;
-        if (g.accumulate) v += ld8(Cp);
-        st8(Cp, v);
       }
+#pragma unroll
+      for (int k = 0; k < BATCH; k++) {
+        const int c = tid + (b0 + k) * NT;
+        const int il = c / CPRW, jl = (c % CPRW) * 8;
+        const int i = i0 + pass * RP + il, j = j0 + jl;
+        if (!(b0 + k < NCH && c < RP * CPRW && i < g.M && j < g.N)) continue;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl + 4);
+        f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const f32x8 bias = bv[NBV == 1 ? 0 : (b0 + k) % NBV];
+        if constexpr (EPI == EPI_STORE || EPI == EPI_F32) v *= g.alpha;
+        if constexpr (EPI == EPI_STORE) {
+          if (use_bias) v += bias;
+          F o;
+#pragma unroll
+          for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e]);
+          st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
+        } else if constexpr (EPI == EPI_GELU) {
+          // the backward needs only gelu' at the pre-activation: store that
+          // (from the fp32 value) next to the activation
+          v += bias;
+          F gu, o;
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float sg = gelu_sigmoid(v[e]);
+            gu[e] = from_f<T>(gelu_tanh_grad_s(v[e], sg));
+            o[e] = from_f<T>(v[e] * sg);
+          }
+          st8(static_cast<T*>(g.aux) + (int64_t)i * g.ldaux + j, gu);
+          st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
+        } else if constexpr (EPI == EPI_RESID) {
+          v += bias;
+          v += x[k];
+          st8(static_cast<float*>(g.C) + (int64_t)i * g.ldc + j, v);
+        } else if constexpr (EPI == EPI_GELU_BWD) {
+          F o;
+#pragma unroll
+          for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e] * to_f<T>(u[k][e]));
+          st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
+        } else {  // EPI_F32
+          float* Cp = static_cast<float*>(g.C) + (int64_t)blockIdx.y * g.split_stride + (int64_t)i * g.ldc + j;
+          if (g.accumulate) v += x[k];
+          st8(Cp, v);
+        }
+      }
+    };
+    if constexpr (BATCH == 1) {
+#pragma unroll 1
+      for (int b0 = 0; b0 < NCH; b0++) chunk_batch(b0);
+    } else {
+#pragma unroll
+      for (int b0 = 0; b0 < NCH; b0 += BATCH) chunk_batch(b0);
     }
   }
 }
