@@ -541,21 +541,22 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   // would not hoist the loads above them by itself).
   constexpr int NCH = (RP * CPRW + NT - 1) / NT;
   constexpr bool HAS_BIAS = EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID;
-  constexpr int NBV = HAS_BIAS ? (NT % CPRW == 0 ? 1 : NCH) : 1;  // distinct bias chunks per thread
-  static_assert(NBV <= 4, "bias chunks per thread");
+  constexpr int NBV0 = NT % CPRW == 0 ? 1 : NCH;  // distinct bias chunks per thread
+  constexpr bool HOIST = HAS_BIAS && NBV0 <= 4;    // (else the bias is loaded with each chunk)
+  constexpr int NBV = HOIST ? NBV0 : 1;
   // (batches measured: one chunk at a time is as fast or faster for gelu',
   // the plain store and the fp32 partials, whose 8-wave kernels spill)
   // (and a thread with several bias chunks takes all its chunks at once, so
   // the bias array is indexed with constants)
-  constexpr int BATCH = EPI == EPI_RESID ? (NCH < 3 ? NCH : 3) : NBV > 1 ? NCH : 1;
-  static_assert(NBV == 1 || BATCH % NBV == 0 || BATCH == NCH, "bias chunk index must be a constant");
+  constexpr int BATCH = NBV > 1 ? NCH : EPI == EPI_RESID ? (NCH < 3 ? NCH : 3) : 1;
+  static_assert(NBV == 1 || BATCH == NCH, "bias chunk index must be a constant");
   const bool use_bias = HAS_BIAS && (EPI != EPI_STORE || g.bias != nullptr);
   f32x8 bv[NBV];
 #pragma unroll
   for (int k = 0; k < NBV; k++) {
     const int j = j0 + ((tid + k * NT) % CPRW) * 8;
     bv[k] = f32x8{};
-    if (use_bias && j < g.N) bv[k] = ld8(g.bias + j);
+    if (HOIST && use_bias && j < g.N) bv[k] = ld8(g.bias + j);
   }
 #pragma unroll 1
   for (int pass = 0; pass < WI; pass++) {
@@ -599,7 +600,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
         const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl);
         const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl + 4);
         f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const f32x8 bias = bv[NBV == 1 ? 0 : (b0 + k) % NBV];
+        const f32x8 bias = HOIST ? bv[NBV == 1 ? 0 : (b0 + k) % NBV] : (use_bias ? ld8(g.bias + j) : f32x8{});
         if constexpr (EPI == EPI_STORE || EPI == EPI_F32) v *= g.alpha;
         if constexpr (EPI == EPI_STORE) {
           if (use_bias) v += bias;
