@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warmup, one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--mode", choices=["train", "eval"], default="train",
+                    help="eval: forward-only validation loss over held-out batches instead of the training step")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -103,6 +105,9 @@ def main():
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(data parallelism is a design note only).", file=sys.stderr)
         sys.exit(2)
+
+    if args.mode == "eval":
+        return run_eval(args)
 
     import numpy as np
     import torch
@@ -242,6 +247,65 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(model, stream, min(args.cpu_sample_tokens, T))
+    print(json.dumps(out), flush=True)
+
+
+def run_eval(args):
+    """Forward-only validation: S held-out micro-batches (a stream of its own
+    seed) through gpt2_eval after W warmup batches; tokens/s of the timed
+    batches, and the mean loss and perplexity they give."""
+    import numpy as np
+    import torch
+
+    from transformer_lm_pretraining_gpt2_amd import binding, evaluation, synth
+    from transformer_lm_pretraining_gpt2_amd.config import CONFIGS, MI355X_BF16_PEAK_FLOPS, MI355X_FP32_MFMA_PEAK_FLOPS
+    from transformer_lm_pretraining_gpt2_amd.config import flops_per_token
+
+    rc = CONFIGS[args.config]
+    model, prec, B, T = rc.model, args.precision or rc.precision, rc.B, rc.T
+    S, W = args.steps, args.warmup
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    step = binding.TrainStep(model, B, T, prec, device=dev)
+    step.set_params(synth.init_params(step.layout, model.n_layer, model.vocab_size))
+    n = synth.stream_length(W + S, 1, B, T)
+    val_seed = synth.DATA_SEED + 1
+    stream = synth.zipf_stream(n, model.vocab_size, val_seed) if rc.data == "zipf" else synth.uniform_stream(
+        n, model.vocab_size, val_seed)
+    mbs = [synth.micro_batch(stream, B, T, i) for i in range(W + S)]
+    d = [(torch.from_numpy(a.reshape(-1)).to(dev), torch.from_numpy(b.reshape(-1)).to(dev)) for a, b in mbs]
+    losses = torch.zeros(W + S, device=dev)
+    for i in range(W):
+        step.evaluate(d[i][0], d[i][1], losses[i:i + 1])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(W, W + S):
+        step.evaluate(d[i][0], d[i][1], losses[i:i + 1])
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    st = step.sync_status()
+    if st != 0:
+        raise SystemExit(f"eval failed: {binding.ERRORS.get(st, st)}")
+    ms = max((t1 - t0) * 1000 / S, ev0.elapsed_time(ev1) / S)
+    tps = B * T / (ms / 1000)
+    fpt = flops_per_token(model, T, causal=True) / 3  # forward only: a third of 6N + 6LTC
+    peak = MI355X_BF16_PEAK_FLOPS if prec == "bf16" else MI355X_FP32_MFMA_PEAK_FLOPS
+    vl = float(np.mean(losses[W:].cpu().numpy().astype(np.float64)))
+    out = {
+        "metric": f"validation tokens/sec (forward-only loss), {args.config} {prec} B={B} T={T}, 1×MI355X",
+        "value": round(tps, 1), "unit": "tokens/s", "n_gpus": 1, "steps": S, "warmup": W,
+        "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "mfu": round(tps * fpt / peak, 4), "flops_per_token": fpt, "dtype": prec,
+        "data": f"synthetic held-out stream: {'Zipf(s=1.0)' if rc.data == 'zipf' else 'uniform'} token ids, "
+                f"seed {val_seed}; random GPT-2 init, seed {synth.INIT_SEED}",
+        "config": {"workload": f"{args.config}: forward-only evaluation of one micro-batch, B={B} T={T}",
+                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "val_loss": round(vl, 4), "perplexity": round(evaluation.perplexity(vl), 2),
+        "val_bpb": None, "val_bpb_note": "bits per byte needs the tokenizer's bytes per token; synthetic ids have none",
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -151,6 +151,17 @@ int gpt2_set_overlap(gpt2_t* h, int enable);
  * gpt2_sync_status (the gather reads row 0 instead). */
 int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, float* d_loss, float* d_loss_rows);
 
+/* Forward-only evaluation of one micro-batch: the same forward and loss as
+ * gpt2_forward (bit for bit), without what only the backward needs (gelu' of
+ * the MLP pre-activation, the embedding sort, dlogits), so gpt2_backward may
+ * not follow it.  The validation readouts of "A small GPT that writes fairy
+ * tales" (training log and Problem 3) are host arithmetic on its mean loss:
+ * perplexity = exp(loss), bits per byte = loss / ln 2 / (bytes per token).
+ *   d_idx, d_targets  int32 [B*T] device; targets required (GPT2_ERR_ARG if NULL)
+ *   d_loss, d_loss_rows  as for gpt2_forward
+ * Token-range errors as for gpt2_forward. */
+int gpt2_eval(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, float* d_loss, float* d_loss_rows);
+
 /* Backward pass of the last forward.  Adds (1/grad_accum_steps) times the
  * gradient of that micro-batch's mean loss into grads; micro_step == 0
  * overwrites grads instead ("Karpathy's four-hour GPT-2 reproduction in one

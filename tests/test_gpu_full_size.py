@@ -60,6 +60,27 @@ def test_full_size_forward_sampled_rows(params):
         assert err <= TOL["bf16"]["rows"]
 
 
+def test_full_size_eval_equals_training_forward(params):
+    # the forward-only path at the benchmark's shapes: same per-position losses
+    # as the training forward, bit for bit (the sampled-rows test above pins
+    # those to the oracle)
+    import torch
+
+    ids, tgt = batches(MODEL, B, T, 1, seed=77)[0]
+    s = binding.TrainStep(MODEL, B, T, "bf16")
+    s.set_params(params)
+    d_ids = torch.from_numpy(ids.reshape(-1)).cuda()
+    d_tgt = torch.from_numpy(tgt.reshape(-1)).cuda()
+    le, lf = torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda")
+    re, rf = torch.zeros(B * T, device="cuda"), torch.zeros(B * T, device="cuda")
+    s.evaluate(d_ids, d_tgt, le, re)
+    s.forward(d_ids, d_tgt, lf, rf)
+    assert s.sync_status() == 0
+    print(f"eval loss {le.item():.6f}, training forward loss {lf.item():.6f}", flush=True)
+    assert le.item() == lf.item()
+    assert torch.equal(re, rf)
+
+
 def test_full_size_step_repeated_sequence(params):
     ids, tgt = batches(MODEL, 1, T, 1, seed=4321)[0]
     rep = (np.repeat(ids, B, axis=0), np.repeat(tgt, B, axis=0))

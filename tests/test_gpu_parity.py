@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 from gpu_common import batches, compare, gpu_step, oracle_step
+from oracle import oracle
 from transformer_lm_pretraining_gpt2_amd import binding, synth
 from transformer_lm_pretraining_gpt2_amd.config import CONFIGS, GPT2Config
 
@@ -172,3 +173,43 @@ def test_overlapped_weight_gradients_match_serial():
     assert a["loss"] == b["loss"]
     for k in ("grads", "params", "m", "v"):
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_eval_matches_forward_and_oracle(prec):
+    # forward-only evaluation: the training forward's loss bit for bit (same
+    # kernels, fewer stores), the oracle's loss to the parity bar, and no
+    # backward allowed after it
+    import torch
+
+    lay = binding.param_layout(PADDED)
+    p0 = synth.random_params(lay, PADDED.vocab_size, seed=8, scale=0.05)
+    (ids, tgt), = batches(PADDED, 2, 128, 1, seed=44)
+    s = binding.TrainStep(PADDED, 2, 128, prec)
+    s.set_params(p0.astype(np.float32))
+    d_ids = torch.from_numpy(ids.reshape(-1).astype(np.int32)).cuda()
+    d_tgt = torch.from_numpy(tgt.reshape(-1).astype(np.int32)).cuda()
+    le, lf = torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda")
+    re, rf = torch.zeros(256, device="cuda"), torch.zeros(256, device="cuda")
+    s.evaluate(d_ids, d_tgt, le, re)
+    with pytest.raises(RuntimeError):
+        s.backward(0, 1)
+    s.forward(d_ids, d_tgt, lf, rf)
+    assert s.sync_status() == 0
+    assert le.item() == lf.item()
+    assert torch.equal(re, rf)
+    rl = np.zeros(256)
+    ref = oracle.fwd_bwd(PADDED, 2, 128, p0, ids, tgt, row_loss=rl)
+    tol = {"fp32": 1e-4, "bf16": 2e-2}[prec]
+    print(f"eval loss gpu {le.item():.6f} oracle {ref:.6f}", flush=True)
+    assert abs(le.item() - ref) <= tol
+    assert np.max(np.abs(re.cpu().numpy() - rl)) <= {"fp32": 1e-4, "bf16": 1e-1}[prec]
+
+
+def test_eval_without_targets_is_rejected():
+    import torch
+
+    s = binding.TrainStep(PADDED, 2, 128, "fp32")
+    d_ids = torch.zeros(256, dtype=torch.int32, device="cuda")
+    with pytest.raises(RuntimeError):
+        s.evaluate(d_ids, None)

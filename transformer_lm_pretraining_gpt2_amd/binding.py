@@ -48,6 +48,7 @@ SIGNATURES = [
     ("gpt2_set_stream", _I, [_P, _P]),
     ("gpt2_set_overlap", _I, [_P, _I]),
     ("gpt2_forward", _I, [_P, _P, _P, _P, _P]),
+    ("gpt2_eval", _I, [_P, _P, _P, _P, _P]),
     ("gpt2_backward", _I, [_P, _I, _I]),
     ("gpt2_adamw_step", _I, [_P, _I, _F, _F, _F, _F, _F, _F, _P]),
     ("gpt2_sync_status", _I, [_P]),
@@ -181,6 +182,11 @@ class TrainStep:
     def forward(self, ids, targets=None, loss=None, loss_rows=None):
         p = lambda t: t.data_ptr() if t is not None else None
         self._check(lib().gpt2_forward(self.h, p(ids), p(targets), p(loss), p(loss_rows)), "forward")
+
+    def evaluate(self, ids, targets, loss=None, loss_rows=None):
+        """Forward-only loss (no backward state kept)."""
+        p = lambda t: t.data_ptr() if t is not None else None
+        self._check(lib().gpt2_eval(self.h, p(ids), p(targets), p(loss), p(loss_rows)), "eval")
 
     def backward(self, micro_step=0, grad_accum_steps=1):
         self._check(lib().gpt2_backward(self.h, micro_step, grad_accum_steps), "backward")

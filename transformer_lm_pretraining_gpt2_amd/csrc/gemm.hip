@@ -619,7 +619,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
             gu[e] = from_f<T>(gelu_tanh_grad_s(v[e], sg));
             o[e] = from_f<T>(v[e] * sg);
           }
-          st8(static_cast<T*>(g.aux) + (int64_t)i * g.ldaux + j, gu);
+          if (g.aux) st8(static_cast<T*>(g.aux) + (int64_t)i * g.ldaux + j, gu);  // (none when evaluating)
           st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
         } else if constexpr (EPI == EPI_RESID) {
           v += bias;

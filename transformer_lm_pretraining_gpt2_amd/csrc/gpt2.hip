@@ -555,7 +555,11 @@ int gpt2_refresh_params(gpt2_t* h) {
   return hip_check(h, to_bf16(h->st, h->params, h->params_lp, h->lay.total), "to_bf16");
 }
 
-int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, float* d_loss, float* d_loss_rows) {
+// The forward of training (train = 1: keeps what the backward needs, gelu'
+// and the embedding sort, and leaves dlogits in place of the logits) or of
+// evaluation (train = 0: loss only).
+static int forward_impl(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, float* d_loss, float* d_loss_rows,
+                        bool train) {
   if (!h || !d_idx) return fail(h, GPT2_ERR_ARG, "null handle or ids");
   const gpt2_config_t& c = h->cfg;
   const int C = c.n_embd, L = c.n_layer, NH = c.n_head, hd = C / NH, Mi = (int)h->M;
@@ -569,7 +573,7 @@ int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, floa
                               c.vocab_size, flags),
                  "embed_fwd");
   if (rc) return rc;
-  if (d_targets) {
+  if (d_targets && train) {
     rc = hip_check(h, embed_sort(h->st, d_idx, Mi, c.vocab_size, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva),
                                  h->w<int32_t>(P.skb), h->w<int32_t>(P.svb), h->w<int32_t>(P.seg), h->w<int32_t>(P.nseg)),
                    "embed_sort");
@@ -605,7 +609,7 @@ int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, floa
     }
     if (rc) return rc;
     g = fwd_args(h, h->w<void>(P.h2[l]), h->W(T_FCW, l), 4 * C, C, h->w<void>(P.g[l]), h->P32(T_FCB, l));
-    g.aux = h->w<void>(P.u[l]);
+    g.aux = train ? h->w<void>(P.u[l]) : nullptr;
     g.ldaux = 4 * C;
     if ((rc = run_gemm(h, K_GEMM_NT_GELU, 0, 0, EPI_GELU, g, "fc"))) return rc;
     g = fwd_args(h, h->w<void>(P.g[l]), h->W(T_FCPW, l), C, 4 * C, h->w<void>(P.x_in[l + 1]), h->P32(T_FCPB, l));
@@ -629,7 +633,7 @@ int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, floa
       Timer t(h, K_CE, 0);
       // dlogits of the mean loss; the 1/K of gradient accumulation is applied in backward
       rc = hip_check(h, cross_entropy(h->st, h->prec, h->w<void>(P.logits), d_targets, rows, Mi, c.vocab_size,
-                                      c.padded_vocab_size, 1.0f / (float)Mx, 1),
+                                      c.padded_vocab_size, 1.0f / (float)Mx, train ? 1 : 0),
                      "cross_entropy");
     }
     if (rc) return rc;
@@ -638,9 +642,18 @@ int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, floa
       if (rc) return rc;
     }
   }
-  h->have_fwd = true;
+  h->have_fwd = train;
   h->fwd_has_targets = d_targets != nullptr;
   return GPT2_OK;
+}
+
+int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, float* d_loss, float* d_loss_rows) {
+  return forward_impl(h, d_idx, d_targets, d_loss, d_loss_rows, true);
+}
+
+int gpt2_eval(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, float* d_loss, float* d_loss_rows) {
+  if (!h || !d_targets) return fail(h, GPT2_ERR_ARG, "evaluation needs targets");
+  return forward_impl(h, d_idx, d_targets, d_loss, d_loss_rows, false);
 }
 
 int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {

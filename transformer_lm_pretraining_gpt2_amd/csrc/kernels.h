@@ -11,7 +11,7 @@ enum Prec { F32 = 0, BF16 = 1 };
 // A(i, r) = A[i*lda + r] (a_t = 0) or A[r*lda + i] (a_t = 1); same for B.
 enum Epi {
   EPI_STORE = 0,    // out (act type) = acc + bias[j]
-  EPI_GELU = 1,     // u = acc + bias[j]; out = gelu_tanh(u), aux = gelu_tanh'(u)   (act type)
+  EPI_GELU = 1,     // u = acc + bias[j]; out = gelu_tanh(u), aux = gelu_tanh'(u)   (act type; no aux if null)
   EPI_RESID = 2,    // out (fp32) = resid (fp32) + acc + bias[j]
   EPI_GELU_BWD = 3, // out (act type) = acc * aux   (aux = gelu_tanh' at the pre-activation)
   EPI_F32 = 4       // out (fp32) = (accumulate ? out : 0) + acc; split s writes out + s*split_stride
@@ -79,8 +79,6 @@ struct ReduceJobs {
   int count;
 };
 hipError_t reduce_jobs(hipStream_t st, const ReduceJob* jobs, int count);
-
-// per-chunk column sums of X [M, N] (act type or fp32) into part [nchunks][N]
 
 // ---- embeddings ----
 hipError_t embed_fwd(hipStream_t st, const int32_t* idx, const int32_t* tgt, const float* wte, const float* wpe,
