@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warmup, one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="activation recompute for the MLP (smaller workspace, one extra pass per layer)")
     ap.add_argument("--mode", choices=["train", "eval"], default="train",
                     help="eval: forward-only validation loss over held-out batches instead of the training step")
     args = ap.parse_args()
@@ -124,7 +126,7 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 
-    step = binding.TrainStep(model, B, T, prec, device=dev)
+    step = binding.TrainStep(model, B, T, prec, device=dev, recompute=args.recompute)
     lay = step.layout
     step.set_params(synth.init_params(lay, model.n_layer, model.vocab_size))
     ISO = 2  # untimed steps after the timed region: the dominant kernel timed without overlap
@@ -238,7 +240,8 @@ def main():
         "config": {"workload": f"{args.config}: one training step (fwd+bwd+clip+AdamW), B={B} T={T} K={K}, "
                                f"L={model.n_layer} nh={model.n_head} C={model.n_embd} V={model.vocab_size}"
                                f"->{model.padded_vocab_size}",
-                   "global_batch": B * K, "seq_len": T, "grad_accum": K, "parallelism": "none (1 GPU)"},
+                   "global_batch": B * K, "seq_len": T, "grad_accum": K, "parallelism": "none (1 GPU)",
+                   "activation_recompute": bool(args.recompute), "workspace_bytes": int(step.workspace.numel())},
         "roofline": roof,
         "loss_first_timed": round(first_loss, 4),
         "loss_last": round(loss.item(), 4),

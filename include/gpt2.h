@@ -54,6 +54,19 @@ typedef struct gpt2_config {
  * ("Reproducing GPT-2 (124M) cheaply with llm.c", setup: mixed precision). */
 typedef enum { GPT2_FP32 = 0, GPT2_BF16 = 1 } gpt2_precision_t;
 
+/* Flag OR'd into the precision argument of gpt2_workspace_bytes and gpt2_init:
+ * activation recompute for the MLP (llm.c's -r option, "Reproducing GPT-2
+ * (124M) cheaply with llm.c", training command flags).  Each layer keeps only
+ * the MLP pre-activation (in the activation type) instead of GELU' and the
+ * GELU output; one GELU-output buffer serves all layers and gpt2_backward
+ * rebuilds it from the pre-activation before each layer's MLP weight
+ * gradient.  The workspace shrinks by (n_layer - 1) * B * T * 4 * n_embd
+ * activation elements; the step costs one extra elementwise pass per layer.
+ * The activation is taken from the rounded pre-activation in this mode, so
+ * bf16 results differ from the default mode within rounding (fp32 results
+ * are identical). */
+#define GPT2_RECOMPUTE_GELU 0x100
+
 enum {
   GPT2_OK = 0,
   GPT2_ERR_CONFIG = -1,      /* shape constraints above violated */

@@ -84,3 +84,16 @@ def test_error_strings_and_kernel_names():
     names = binding.kernel_names()
     assert "gemm_nt_store" in names and "attn_fwd" in names and "adamw" in names
     assert L.gpt2_kernel_name(len(names)) is None
+
+
+def test_recompute_flag_shrinks_the_workspace():
+    # one GELU-output buffer for all layers instead of one per layer
+    m = CONFIGS["gpt2_124m"].model
+    B, T = CONFIGS["gpt2_124m"].B, CONFIGS["gpt2_124m"].T
+    for prec, a in ((binding.GPT2_BF16, 2), (binding.GPT2_FP32, 4)):
+        full = binding.workspace_bytes(m, B, T, prec)
+        rc = binding.workspace_bytes(m, B, T, prec | binding.GPT2_RECOMPUTE_GELU)
+        assert full - rc == (m.n_layer - 1) * B * T * 4 * m.n_embd * a
+    # a flag without a valid precision, or an unknown bit, is an argument error
+    assert binding.workspace_bytes(m, B, T, 2 | binding.GPT2_RECOMPUTE_GELU) == -3  # GPT2_ERR_ARG
+    assert binding.workspace_bytes(m, B, T, binding.GPT2_BF16 | 0x200) == -3  # GPT2_ERR_ARG

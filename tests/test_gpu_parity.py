@@ -213,3 +213,30 @@ def test_eval_without_targets_is_rejected():
     d_ids = torch.zeros(256, dtype=torch.int32, device="cuda")
     with pytest.raises(RuntimeError):
         s.evaluate(d_ids, None)
+
+
+def test_recompute_fp32_identical_to_default():
+    # fp32: rounding the pre-activation to the act type is the identity, so the
+    # recompute mode reproduces the default step bit for bit (loss, gradients,
+    # updated parameters), which also pins the backward's rebuilt activations
+    # to the forward's
+    lay = binding.param_layout(SMALL)
+    p0 = synth.init_params(lay, SMALL.n_layer, SMALL.vocab_size, dtype=np.float64)
+    mb = batches(SMALL, 4, 256, 2, seed=12)
+    a = gpu_step(SMALL, 4, 256, "fp32", p0, mb)
+    b = gpu_step(SMALL, 4, 256, "fp32", p0, mb, handle=binding.TrainStep(SMALL, 4, 256, "fp32", recompute=True))
+    assert a["loss"] == b["loss"]
+    for k in ("grads", "params", "m", "v"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_recompute_bf16_matches_oracle():
+    # bf16: the activation comes from the rounded pre-activation; the step
+    # still meets the parity bar (4 layers, so three layers are rebuilt)
+    lay = binding.param_layout(SMALL)
+    p0 = synth.init_params(lay, SMALL.n_layer, SMALL.vocab_size, dtype=np.float64)
+    mb = batches(SMALL, 8, 256, 1, seed=99)
+    g = gpu_step(SMALL, 8, 256, "bf16", p0, mb, lr=1e-3,
+                 handle=binding.TrainStep(SMALL, 8, 256, "bf16", recompute=True))
+    o = oracle_step(SMALL, p0, mb, lr=1e-3)
+    compare(SMALL, g, o, "bf16")

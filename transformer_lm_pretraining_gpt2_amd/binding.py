@@ -13,6 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgpt2mi.so")
 
 GPT2_FP32, GPT2_BF16 = 0, 1
+GPT2_RECOMPUTE_GELU = 0x100  # OR into the precision: MLP activation recompute
 ERRORS = {0: "GPT2_OK", -1: "GPT2_ERR_CONFIG", -2: "GPT2_ERR_SHAPE", -3: "GPT2_ERR_ARG", -4: "GPT2_ERR_HIP",
           -5: "GPT2_ERR_TOKEN_RANGE", -6: "GPT2_ERR_NONFINITE", -7: "GPT2_ERR_WORKSPACE"}
 
@@ -130,16 +131,18 @@ class TrainStep:
     bf16 copy (bf16 precision only); workspace is a uint8 tensor.
     """
 
-    def __init__(self, model, B, T, precision, device="cuda", stream=None):
+    def __init__(self, model, B, T, precision, device="cuda", stream=None, recompute=False):
         import torch
 
         self.torch = torch
         self.model, self.B, self.T = model, B, T
         self.precision = GPT2_BF16 if precision in ("bf16", GPT2_BF16) else GPT2_FP32
+        self.recompute = bool(recompute)
+        flags = self.precision | (GPT2_RECOMPUTE_GELU if self.recompute else 0)
         self.N = num_params(model)
         if self.N < 0:
             raise Gpt2Error(self.N, "invalid config")
-        ws = workspace_bytes(model, B, T, self.precision)
+        ws = workspace_bytes(model, B, T, flags)
         if ws < 0:
             raise Gpt2Error(ws, "invalid shapes")
         f32 = dict(dtype=torch.float32, device=device)
@@ -152,7 +155,7 @@ class TrainStep:
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         self.layout = param_layout(model)
         h = ctypes.c_void_p()
-        rc = lib().gpt2_init(ctypes.byref(h), ctypes.byref(cconfig(model)), self.precision, B, T,
+        rc = lib().gpt2_init(ctypes.byref(h), ctypes.byref(cconfig(model)), flags, B, T,
                              self.params.data_ptr(), self.params_lp.data_ptr() if self.params_lp is not None else None,
                              self.grads.data_ptr(), self.m.data_ptr(), self.v.data_ptr(), self.workspace.data_ptr(),
                              ws, self.stream.cuda_stream)

@@ -613,11 +613,21 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
           // (from the fp32 value) next to the activation
           v += bias;
           F gu, o;
+          if (g.preact) {
+            // keep the rounded pre-activation; the activation comes from that
+            // same rounded value, so recomputing it later reproduces it exactly
 #pragma unroll
-          for (int e = 0; e < 8; e++) {
-            const float sg = gelu_sigmoid(v[e]);
-            gu[e] = from_f<T>(gelu_tanh_grad_s(v[e], sg));
-            o[e] = from_f<T>(v[e] * sg);
+            for (int e = 0; e < 8; e++) {
+              gu[e] = from_f<T>(v[e]);
+              o[e] = from_f<T>(gelu_tanh(to_f<T>(gu[e])));
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+              const float sg = gelu_sigmoid(v[e]);
+              gu[e] = from_f<T>(gelu_tanh_grad_s(v[e], sg));
+              o[e] = from_f<T>(v[e] * sg);
+            }
           }
           if (g.aux) st8(static_cast<T*>(g.aux) + (int64_t)i * g.ldaux + j, gu);  // (none when evaluating)
           st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
@@ -627,8 +637,16 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
           st8(static_cast<float*>(g.C) + (int64_t)i * g.ldc + j, v);
         } else if constexpr (EPI == EPI_GELU_BWD) {
           F o;
+          if (g.preact) {
 #pragma unroll
-          for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e] * to_f<T>(u[k][e]));
+            for (int e = 0; e < 8; e++) {
+              const float x = to_f<T>(u[k][e]);
+              o[e] = from_f<T>(v[e] * gelu_tanh_grad_s(x, gelu_sigmoid(x)));
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e] * to_f<T>(u[k][e]));
+          }
           st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
         } else {  // EPI_F32
           float* Cp = static_cast<float*>(g.C) + (int64_t)blockIdx.y * g.split_stride + (int64_t)i * g.ldc + j;

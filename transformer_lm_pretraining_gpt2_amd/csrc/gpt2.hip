@@ -120,6 +120,8 @@ struct Plan {
 Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
   Plan P;
   const int64_t M = (int64_t)B * T, C = c.n_embd, L = c.n_layer, NH = c.n_head;
+  const bool recompute = (prec & GPT2_RECOMPUTE_GELU) != 0;
+  prec &= ~GPT2_RECOMPUTE_GELU;
   const int64_t a = prec == GPT2_BF16 ? 2 : 4;
   auto take = [&](int64_t bytes) {
     const int64_t off = P.bytes;
@@ -139,7 +141,8 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
     P.atty.push_back(take(a * M * C));
     P.lse.push_back(take(4 * M * NH));
     P.u.push_back(take(a * M * 4 * C));
-    P.g.push_back(take(a * M * 4 * C));
+    // with activation recompute every layer's GELU output shares layer 0's buffer
+    P.g.push_back(recompute && l > 0 ? P.g[0] : take(a * M * 4 * C));
   }
   P.hf = take(a * M * C);
   P.meanf = take(4 * M);
@@ -203,6 +206,7 @@ struct gpt2_handle {
   // or reads their partial sums.
   hipStream_t side = nullptr;
   bool overlap = true;
+  bool recompute = false;  // GPT2_RECOMPUTE_GELU: the layers share one GELU-output buffer
   hipEvent_t ev_fork = nullptr, ev_done[4] = {nullptr, nullptr, nullptr, nullptr};
   Layout lay;
   Plan plan;
@@ -467,7 +471,8 @@ int gpt2_check_shapes(const gpt2_config_t* cfg, int B, int T) {
 int64_t gpt2_workspace_bytes(const gpt2_config_t* cfg, int B, int T, int precision) {
   int rc = gpt2_check_shapes(cfg, B, T);
   if (rc) return rc;
-  if (precision != GPT2_FP32 && precision != GPT2_BF16) return GPT2_ERR_ARG;
+  const int base = precision & ~GPT2_RECOMPUTE_GELU;
+  if (base != GPT2_FP32 && base != GPT2_BF16) return GPT2_ERR_ARG;
   return make_plan(*cfg, B, T, precision).bytes;
 }
 
@@ -477,22 +482,25 @@ int gpt2_init(gpt2_t** out, const gpt2_config_t* cfg, int precision, int B, int 
   *out = nullptr;
   int rc = gpt2_check_shapes(cfg, B, T);
   if (rc) return rc;
-  if (precision != GPT2_FP32 && precision != GPT2_BF16) return GPT2_ERR_ARG;
+  const bool recompute = (precision & GPT2_RECOMPUTE_GELU) != 0;
+  const int base = precision & ~GPT2_RECOMPUTE_GELU;
+  if (base != GPT2_FP32 && base != GPT2_BF16) return GPT2_ERR_ARG;
   auto aligned = [](const void* p) { return p && (reinterpret_cast<uintptr_t>(p) % 256) == 0; };
   if (!aligned(params) || !aligned(grads) || !aligned(adam_m) || !aligned(adam_v) || !aligned(workspace))
     return GPT2_ERR_ARG;
-  if (precision == GPT2_BF16 && !aligned(params_lp)) return GPT2_ERR_ARG;
+  if (base == GPT2_BF16 && !aligned(params_lp)) return GPT2_ERR_ARG;
   Plan plan = make_plan(*cfg, B, T, precision);
   if (workspace_bytes < plan.bytes) return GPT2_ERR_WORKSPACE;
   gpt2_t* h = new (std::nothrow) gpt2_handle();
   if (!h) return GPT2_ERR_ARG;
   h->cfg = *cfg;
-  h->prec = precision == GPT2_BF16 ? BF16 : F32;
+  h->prec = base == GPT2_BF16 ? BF16 : F32;
+  h->recompute = recompute;
   h->B = B;
   h->T = T;
   h->M = (int64_t)B * T;
   h->params = params;
-  h->params_lp = precision == GPT2_BF16 ? params_lp : nullptr;
+  h->params_lp = base == GPT2_BF16 ? params_lp : nullptr;
   h->grads = grads;
   h->m = adam_m;
   h->v = adam_v;
@@ -611,6 +619,7 @@ static int forward_impl(gpt2_t* h, const int32_t* d_idx, const int32_t* d_target
     g = fwd_args(h, h->w<void>(P.h2[l]), h->W(T_FCW, l), 4 * C, C, h->w<void>(P.g[l]), h->P32(T_FCB, l));
     g.aux = train ? h->w<void>(P.u[l]) : nullptr;
     g.ldaux = 4 * C;
+    g.preact = h->recompute;  // (in evaluation too, so its loss equals the training forward's)
     if ((rc = run_gemm(h, K_GEMM_NT_GELU, 0, 0, EPI_GELU, g, "fc"))) return rc;
     g = fwd_args(h, h->w<void>(P.g[l]), h->W(T_FCPW, l), C, 4 * C, h->w<void>(P.x_in[l + 1]), h->P32(T_FCPB, l));
     g.resid = h->w<float>(P.x_mid[l]);
@@ -696,6 +705,13 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     return rc;
 
   for (int l = L - 1; l >= 0; l--) {
+    // activation recompute: rebuild this layer's GELU output in the shared
+    // buffer (the last layer's is still there from the forward); the previous
+    // layer's readers of that buffer were joined before its reduction flush
+    if (h->recompute && l < L - 1) {
+      rc = hip_check(h, gelu_fwd(h->st, h->prec, h->w<void>(P.u[l]), h->w<void>(P.g[l]), h->M * 4 * C), "gelu recompute");
+      if (rc) return rc;
+    }
     // MLP down-projection: dres is the gradient of the block output
     if ((rc = side_weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), 3,
                                acc, "fcproj dw")))
@@ -703,6 +719,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     g = dx_args(h, dres_op, h->W(T_FCPW, l), C, 4 * C, h->w<void>(P.du));
     g.aux = h->w<void>(P.u[l]);
     g.ldaux = 4 * C;
+    g.preact = h->recompute;
     if ((rc = run_gemm(h, K_GEMM_NN_GELU_BWD, 0, 1, EPI_GELU_BWD, g, "fcproj dx"))) return rc;
     // MLP up-projection
     if ((rc = side_weight_grad(h, h->w<void>(P.du), h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), h->G32(T_FCB, l),

@@ -12,8 +12,10 @@ enum Prec { F32 = 0, BF16 = 1 };
 enum Epi {
   EPI_STORE = 0,    // out (act type) = acc + bias[j]
   EPI_GELU = 1,     // u = acc + bias[j]; out = gelu_tanh(u), aux = gelu_tanh'(u)   (act type; no aux if null)
+                    //   preact: aux = u rounded to the act type, out = gelu_tanh(that rounded u)
   EPI_RESID = 2,    // out (fp32) = resid (fp32) + acc + bias[j]
   EPI_GELU_BWD = 3, // out (act type) = acc * aux   (aux = gelu_tanh' at the pre-activation)
+                    //   preact: aux = the pre-activation u, out = acc * gelu_tanh'(u)
   EPI_F32 = 4       // out (fp32) = (accumulate ? out : 0) + acc; split s writes out + s*split_stride
 };
 
@@ -34,6 +36,7 @@ struct GemmArgs {
   int splits = 1;
   int64_t split_stride = 0;
   float alpha = 1.f;  // EPI_STORE / EPI_F32: acc is scaled by alpha before the bias / accumulation
+  int preact = 0;     // EPI_GELU / EPI_GELU_BWD: aux holds the pre-activation (activation recompute)
   // EPI_F32 with a_t = 1 only: when set, the blocks of the first column tile also
   // write sum_r A(i, r) over their reduction range to colsum[split*colsum_stride + i]
   // (the bias gradient of a weight-gradient product, before the split reduction)
@@ -107,5 +110,7 @@ hipError_t adamw(hipStream_t st, float* p, const float* g, float* m, float* v, v
                  const int* skip);
 // bf16 copy of fp32 values
 hipError_t to_bf16(hipStream_t st, const float* src, void* dst, int64_t n);
+// out = gelu_tanh(u) elementwise in the act type (n a multiple of 8)
+hipError_t gelu_fwd(hipStream_t st, Prec p, const void* u, void* out, int64_t n);
 
 }  // namespace gpt2k

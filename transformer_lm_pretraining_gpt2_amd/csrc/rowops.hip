@@ -624,6 +624,21 @@ __global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ p, const
   }
 }
 
+// gelu of a stored pre-activation (activation recompute): the same function of
+// the same rounded values as the forward's GELU epilogue, so the result is the
+// forward's activation bit for bit
+template <typename T>
+__global__ void __launch_bounds__(256) gelu_fwd_kernel(const T* __restrict__ u, T* __restrict__ out, int64_t n8) {
+  typedef typename Frag<T>::type F;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    const F x = ld8(u + i * 8);
+    F o;
+#pragma unroll
+    for (int e = 0; e < 8; e++) o[e] = from_f<T>(gelu_tanh(to_f<T>(x[e])));
+    st8(out + i * 8, o);
+  }
+}
+
 __global__ void to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__ dst, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     dst[i] = (bf16)src[i];
@@ -784,6 +799,19 @@ hipError_t adamw(hipStream_t st, float* p, const float* g, float* m, float* v, v
   const unsigned blocks = (unsigned)std::min<int64_t>((nq + 255) / 256, 1 << 30);
   hipLaunchKernelGGL(adamw_kernel, dim3(blocks), dim3(256), 0, st, p, g, m, v, static_cast<bf16*>(p_lp), nq, n_decay, lr,
                      b1, b2, eps, wd, 1.f / bc1, 1.f / bc2, scale, flags);
+  return hipGetLastError();
+}
+
+hipError_t gelu_fwd(hipStream_t st, Prec p, const void* u, void* out, int64_t n) {
+  if (n % 8 != 0) return hipErrorInvalidValue;
+  const int64_t n8 = n / 8;
+  const unsigned blocks = (unsigned)std::min<int64_t>((n8 + 255) / 256, 4096);
+  if (p == BF16)
+    hipLaunchKernelGGL(gelu_fwd_kernel<bf16>, dim3(blocks), dim3(256), 0, st, static_cast<const bf16*>(u),
+                       static_cast<bf16*>(out), n8);
+  else
+    hipLaunchKernelGGL(gelu_fwd_kernel<float>, dim3(blocks), dim3(256), 0, st, static_cast<const float*>(u),
+                       static_cast<float*>(out), n8);
   return hipGetLastError();
 }
 
