@@ -98,6 +98,8 @@ def main():
                     help="before warmup, one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--recompute", action="store_true",
                     help="activation recompute for the MLP (smaller workspace, one extra pass per layer)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="forward products on FP8 E4M3 copies (per-row scales); reported as its own dtype")
     ap.add_argument("--mode", choices=["train", "eval"], default="train",
                     help="eval: forward-only validation loss over held-out batches instead of the training step")
     args = ap.parse_args()
@@ -126,7 +128,7 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
 
-    step = binding.TrainStep(model, B, T, prec, device=dev, recompute=args.recompute)
+    step = binding.TrainStep(model, B, T, prec, device=dev, recompute=args.recompute, fp8=args.fp8)
     lay = step.layout
     step.set_params(synth.init_params(lay, model.n_layer, model.vocab_size))
     ISO = 2  # untimed steps after the timed region: the dominant kernel timed without overlap
@@ -220,7 +222,8 @@ def main():
                                 "note": "same kernel, overlap off, untimed steps after the timed region"}
 
     out = {
-        "metric": METRIC if args.config == "gpt2_124m" else f"training tokens/sec + MFU, {args.config}",
+        "metric": (METRIC if args.config == "gpt2_124m" and not args.fp8 else
+                   f"training tokens/sec + MFU, {args.config}" + (" (FP8 E4M3 forward products)" if args.fp8 else "")),
         "value": round(tps, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -234,14 +237,15 @@ def main():
         "tflops": round(tps * fpt / 1e12, 1),
         "flops_per_token": fpt,
         "flops_per_token_noncausal": flops_per_token(model, T, causal=False),
-        "dtype": prec,
+        "dtype": "fp8 e4m3 forward products, bf16 backward" if args.fp8 else prec,
         "data": f"synthetic: {'Zipf(s=1.0)' if rc.data == 'zipf' else 'uniform'} token ids over {model.vocab_size}, "
                 f"seed {synth.DATA_SEED}; random GPT-2 init, seed {synth.INIT_SEED}",
         "config": {"workload": f"{args.config}: one training step (fwd+bwd+clip+AdamW), B={B} T={T} K={K}, "
                                f"L={model.n_layer} nh={model.n_head} C={model.n_embd} V={model.vocab_size}"
                                f"->{model.padded_vocab_size}",
                    "global_batch": B * K, "seq_len": T, "grad_accum": K, "parallelism": "none (1 GPU)",
-                   "activation_recompute": bool(args.recompute), "workspace_bytes": int(step.workspace.numel())},
+                   "activation_recompute": bool(args.recompute), "fp8_forward": bool(args.fp8),
+                   "workspace_bytes": int(step.workspace.numel())},
         "roofline": roof,
         "loss_first_timed": round(first_loss, 4),
         "loss_last": round(loss.item(), 4),

@@ -67,6 +67,18 @@ typedef enum { GPT2_FP32 = 0, GPT2_BF16 = 1 } gpt2_precision_t;
  * are identical). */
 #define GPT2_RECOMPUTE_GELU 0x100
 
+/* Flag OR'd into the precision (GPT2_BF16 only): the forward's matmuls (qkv,
+ * attention projection, MLP up and down, tied head) take FP8 E4M3 operands on
+ * gfx950's FP8 matrix cores ("Reproducing GPT-2 (124M) cheaply with llm.c",
+ * where FP8 training is announced as the next step), accumulating in fp32.
+ * Scaling is per row: each activation row (token) and each weight row
+ * (output channel) is stored as E4M3 values times one fp32 scale,
+ * scale = max |row| / 448.  The backward stays bf16 (on the bf16 activations
+ * and weights).  The workspace grows by the FP8 weight copy (one byte per
+ * parameter), its row scales and one FP8 activation buffer of B*T*4*n_embd
+ * bytes. */
+#define GPT2_FP8_FWD 0x200
+
 enum {
   GPT2_OK = 0,
   GPT2_ERR_CONFIG = -1,      /* shape constraints above violated */

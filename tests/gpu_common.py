@@ -85,8 +85,18 @@ def batches(model, B, T, K, seed, data="zipf", index0=0):
 # Parity bar: fp32 mode |loss diff| <= 1e-4 and per-tensor gradient relative
 # L2 <= 1e-4; bf16 mode |loss diff| <= 2e-2, parameter and per-tensor gradient
 # relative L2 <= 3e-2 after one step.  Per-position losses: 1e-4 / 1e-1.
+# FP8 forward products (bf16 backward): an E4M3 value keeps 4 significant
+# bits, so rounding to nearest errs by at most 2^-4 relative (RMS about 2.4 %
+# over a binade); a product of two such operands summed over K random-sign
+# terms errs by about sqrt(2) * 2.4 % = 3.4 % of its RMS.  Every gradient
+# passes through several such products and 12 layers of FP8 forward
+# activations, so per-tensor gradients land some 5-10 % from the exact ones
+# (measured 6 % at 4 layers, 8.6 % at 124M); the bar is 0.2, well below the
+# 100 % of a dropped scale or a transposed operand.  The loss moves by the
+# logits' perturbation (measured 2e-3 to 6e-3): bar 5e-2.
 TOL = {"fp32": dict(loss=1e-4, grad=1e-4, param=1e-4, rows=1e-4),
-       "bf16": dict(loss=2e-2, grad=3e-2, param=3e-2, rows=1e-1)}
+       "bf16": dict(loss=2e-2, grad=3e-2, param=3e-2, rows=1e-1),
+       "fp8": dict(loss=5e-2, grad=2e-1, param=5e-2, rows=2e-1)}
 
 
 def compare(model, g, o, prec, check_rows=True):

@@ -96,4 +96,21 @@ def test_recompute_flag_shrinks_the_workspace():
         assert full - rc == (m.n_layer - 1) * B * T * 4 * m.n_embd * a
     # a flag without a valid precision, or an unknown bit, is an argument error
     assert binding.workspace_bytes(m, B, T, 2 | binding.GPT2_RECOMPUTE_GELU) == -3  # GPT2_ERR_ARG
-    assert binding.workspace_bytes(m, B, T, binding.GPT2_BF16 | 0x200) == -3  # GPT2_ERR_ARG
+    assert binding.workspace_bytes(m, B, T, binding.GPT2_BF16 | 0x400) == -3  # GPT2_ERR_ARG
+
+
+def test_fp8_flag_workspace():
+    # FP8 forward products: one byte per parameter for the weights' FP8 copy,
+    # a scale per weight row (tied head + four matrices per layer), one FP8
+    # activation buffer [B*T, 4C] and its row scales (each buffer 256-B aligned)
+    m = CONFIGS["gpt2_124m"].model
+    B, T = CONFIGS["gpt2_124m"].B, CONFIGS["gpt2_124m"].T
+    up = lambda n: (n + 255) // 256 * 256
+    extra = (up(num_params(m)) + up(4 * (m.padded_vocab_size + m.n_layer * 9 * m.n_embd)) + up(B * T * 4 * m.n_embd)
+             + up(4 * B * T))
+    full = binding.workspace_bytes(m, B, T, binding.GPT2_BF16)
+    assert binding.workspace_bytes(m, B, T, binding.GPT2_BF16 | binding.GPT2_FP8_FWD) - full == extra
+    # bf16 only, and the fused FP8 layer-norm output needs a width that is a multiple of 256
+    assert binding.workspace_bytes(m, B, T, binding.GPT2_FP32 | binding.GPT2_FP8_FWD) == -3
+    narrow = GPT2Config(vocab_size=509, padded_vocab_size=512, n_layer=2, n_head=4, n_embd=128, max_seq_len=128)
+    assert binding.workspace_bytes(narrow, 2, 128, binding.GPT2_BF16 | binding.GPT2_FP8_FWD) == -3

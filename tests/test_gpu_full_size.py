@@ -124,6 +124,19 @@ def test_full_size_recompute_step_repeated_sequence(params):
     compare(MODEL, g, o, "bf16")
 
 
+def test_full_size_fp8_step_repeated_sequence(params):
+    # FP8 forward products at the benchmark's shapes, against the oracle
+    ids, tgt = batches(MODEL, 1, T, 1, seed=2468)[0]
+    rep = (np.repeat(ids, B, axis=0), np.repeat(tgt, B, axis=0))
+    print("gpu step with FP8 forward products (B=16, T=1024)", flush=True)
+    g = gpu_step(MODEL, B, T, "bf16", params, [rep], handle=binding.TrainStep(MODEL, B, T, "bf16", fp8=True))
+    print("oracle step (B=1, T=1024, fp32)", flush=True)
+    o = oracle_step(MODEL, params, [(ids, tgt)], R=np.float32)
+    g["rows"] = [g["rows"][0][k * T:(k + 1) * T] for k in range(B)]
+    o["rows"] = [o["rows"][0]] * B
+    compare(MODEL, g, o, "fp8")
+
+
 def test_story_config_launch_shape():
     # story-scale GPT (27.6M params: V 4096, L 8, nh 8, C 512) at its own B = 64, T = 512
     rc = CONFIGS["story"]

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libgpt2mi.so")
 
 GPT2_FP32, GPT2_BF16 = 0, 1
 GPT2_RECOMPUTE_GELU = 0x100  # OR into the precision: MLP activation recompute
+GPT2_FP8_FWD = 0x200  # OR into the precision (bf16 only): forward products on FP8 E4M3 copies
 ERRORS = {0: "GPT2_OK", -1: "GPT2_ERR_CONFIG", -2: "GPT2_ERR_SHAPE", -3: "GPT2_ERR_ARG", -4: "GPT2_ERR_HIP",
           -5: "GPT2_ERR_TOKEN_RANGE", -6: "GPT2_ERR_NONFINITE", -7: "GPT2_ERR_WORKSPACE"}
 
@@ -131,14 +132,15 @@ class TrainStep:
     bf16 copy (bf16 precision only); workspace is a uint8 tensor.
     """
 
-    def __init__(self, model, B, T, precision, device="cuda", stream=None, recompute=False):
+    def __init__(self, model, B, T, precision, device="cuda", stream=None, recompute=False, fp8=False):
         import torch
 
         self.torch = torch
         self.model, self.B, self.T = model, B, T
         self.precision = GPT2_BF16 if precision in ("bf16", GPT2_BF16) else GPT2_FP32
         self.recompute = bool(recompute)
-        flags = self.precision | (GPT2_RECOMPUTE_GELU if self.recompute else 0)
+        self.fp8 = bool(fp8)
+        flags = self.precision | (GPT2_RECOMPUTE_GELU if self.recompute else 0) | (GPT2_FP8_FWD if self.fp8 else 0)
         self.N = num_params(model)
         if self.N < 0:
             raise Gpt2Error(self.N, "invalid config")

@@ -10,11 +10,20 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// FP8 E4M3 (OCP encoding on gfx950) values are stored as bytes.
+typedef unsigned char fp8e4;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 // Eight consecutive elements along a matmul's reduction dimension: the
-// per-lane operand of one (virtual) 32x32x16 MFMA step.
+// per-lane operand of one (virtual) 32x32x16 MFMA step.  FP8: 32 consecutive
+// elements, the per-lane operand of one 32x32x64 MFMA.
 template <typename T> struct Frag;
 template <> struct Frag<bf16> { typedef bf16x8 type; };
 template <> struct Frag<float> { typedef f32x8 type; };
+template <> struct Frag<fp8e4> { typedef i32x8 type; };
+// reduction depth of one MFMA step for an operand type
+template <typename T> struct KStep { static constexpr int k = 16; };
+template <> struct KStep<fp8e4> { static constexpr int k = 64; };
 
 // Four consecutive output elements (one lane's run in a 32x32 accumulator).
 template <typename T> struct Quad;
@@ -46,6 +55,11 @@ __device__ __forceinline__ void mma16(f32x16& acc, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mma16(f32x16& acc, f32x8 a, f32x8 b) {
 #pragma unroll
   for (int s = 0; s < 8; s++) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc, 0, 0, 0);
+}
+// FP8 E4M3 x E4M3: one 32x32x64 MFMA (block scales 2^0); each lane supplies 32
+// reduction values, the same 32 slots for both operands, so all 64 are summed.
+__device__ __forceinline__ void mma16(f32x16& acc, i32x8 a, i32x8 b) {
+  acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
 }
 
 template <typename T> __device__ __forceinline__ float to_f(T x) { return (float)x; }

@@ -21,6 +21,7 @@ namespace {
 template <typename T> struct Vec16;  // 16 bytes of T
 template <> struct Vec16<bf16> { typedef bf16x8 type; static constexpr int n = 8; };
 template <> struct Vec16<float> { typedef f32x4 type; static constexpr int n = 4; };
+template <> struct Vec16<fp8e4> { typedef f32x4 type; static constexpr int n = 16; };
 
 // One operand tile (R output rows x BK reduction) on its way global ->
 // registers -> LDS, and the MFMA fragments read back from LDS.
@@ -104,7 +105,14 @@ struct Operand {
   // Fragment of substep ks for rows rb .. rb+31: lane l gets row rb + l%32 and
   // reduction values 16*ks + 8*(l/32) + 0..7.
   static __device__ __forceinline__ F frag(const T* s, int rb, int ks, int lane) {
-    if constexpr (TRANS == 0) {
+    if constexpr (sizeof(T) == 1) {
+      // FP8: 32 values (two 16-byte reads) at reduction offset 64*ks + 32*(l/32)
+      static_assert(TRANS == 0, "FP8 operands must be reduction-contiguous");
+      const T* p = s + (rb + (lane & 31)) * LD + ks * 64 + 32 * (lane >> 5);
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 16);
+      return __builtin_bit_cast(F, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else if constexpr (TRANS == 0) {
       return ld8(s + (rb + (lane & 31)) * LD + ks * 16 + 8 * (lane >> 5));
     } else if constexpr (sizeof(T) == 2) {
       // within each 16-lane group, lane j points at row r0 + j/4, columns
@@ -287,14 +295,22 @@ constexpr bool gemm_has_colsum(int at, int epi, int waves) { return at == 1 && e
 // NBUF = 0: operands staged through registers (two register stages, two LDS
 // buffers).  NBUF >= 2 (bf16): direct-to-LDS loads into a ring of NBUF LDS
 // buffers, the tile NBUF steps ahead loading while the current one is used.
-template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI, int NBUF>
+// TIn: operand type (T, or FP8 E4M3 with T = bf16 outputs: reduction-
+// contiguous operands, register staging, acc(i, j) scaled by scale_a[i] *
+// scale_b[j] before the epilogue).
+template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI, int NBUF, typename TIn>
 __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   constexpr int NT = WI * WJ * 64;
   constexpr int WTI = BM / WI, WTJ = BN / WJ;
   constexpr int TI = WTI / 32, TJ = WTJ / 32;
-  typedef Operand<T, BM, BK, NT, AT> OA;
-  typedef Operand<T, BN, BK, NT, BT> OB;
-  typedef typename Frag<T>::type F;
+  constexpr bool FP8 = sizeof(TIn) == 1;
+  constexpr int KS = KStep<TIn>::k;  // reduction depth of one MFMA step
+  constexpr int NSUB = BK / KS;      // MFMA steps per LDS tile
+  static_assert(!FP8 || (AT == 0 && BT == 0 && NBUF == 0), "FP8: reduction-contiguous operands, register staging");
+  typedef Operand<TIn, BM, BK, NT, AT> OA;
+  typedef Operand<TIn, BN, BK, NT, BT> OB;
+  typedef typename Frag<TIn>::type FI;  // operand fragments
+  typedef typename Frag<T>::type F;     // eight output values
   typedef typename Quad<T>::type Q;
   // Operand tiles (two buffers each) and, after the main loop, the epilogue's
   // staging area for half of the output tile (fp32) share one LDS block.
@@ -303,11 +319,11 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   typedef DtlOperand<BM, BK, WI * WJ, AT> DA;
   typedef DtlOperand<BN, BK, WI * WJ, BT> DB;
   constexpr int DSTAGE = (BM + BN) * BK * 2;  // one ring buffer (both operands)
-  constexpr int OPER_BYTES = NBUF ? NBUF * DSTAGE : 2 * (OA::ELEMS + OB::ELEMS) * (int)sizeof(T);
+  constexpr int OPER_BYTES = NBUF ? NBUF * DSTAGE : 2 * (OA::ELEMS + OB::ELEMS) * (int)sizeof(TIn);
   constexpr int STAGE_BYTES = RP * SLD * 4;
   __shared__ __attribute__((aligned(16))) char smem[OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES];
-  T (*sA)[OA::ELEMS] = reinterpret_cast<T (*)[OA::ELEMS]>(smem);
-  T (*sB)[OB::ELEMS] = reinterpret_cast<T (*)[OB::ELEMS]>(smem + 2 * OA::ELEMS * sizeof(T));
+  TIn (*sA)[OA::ELEMS] = reinterpret_cast<TIn (*)[OA::ELEMS]>(smem);
+  TIn (*sB)[OB::ELEMS] = reinterpret_cast<TIn (*)[OB::ELEMS]>(smem + 2 * OA::ELEMS * sizeof(TIn));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wi = wave / WJ, wj = wave % WJ;
@@ -325,8 +341,8 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   const int kchunk = g.K / g.splits;
   const int kbeg = blockIdx.y * kchunk;
   const int nk = kchunk / BK;
-  const T* A = static_cast<const T*>(g.A);
-  const T* Bm = static_cast<const T*>(g.B);
+  const TIn* A = static_cast<const TIn*>(g.A);
+  const TIn* Bm = static_cast<const TIn*>(g.B);
 
   f32x16 acc[TI][TJ];
 #pragma unroll
@@ -341,12 +357,12 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   // more than the overlap wins).  CSV = 1 also accumulates the bias gradient
   // sum_r A(i, r) from the A fragments: each lane adds its 8 reduction values
   // per fragment in a fixed order.
-  constexpr bool PIPE = AT == 0;
+  constexpr bool PIPE = AT == 0 && !FP8;  // (FP8 fragments are twice as wide: no room for a second set)
   // With BK = 64 (four substeps per tile) the next tile's LDS stores are
   // spread over the substeps, overlapping them with the MFMAs (they fill the
   // other buffer, which the barrier after the tile protects); with two
   // substeps the spread costs more than it hides.
-  constexpr bool ILV = BK / 16 >= 4;
+  constexpr bool ILV = NSUB >= 4;
   constexpr bool HAS_CS = gemm_has_colsum(AT, EPI, WI * WJ);
 #define GEMM_FRAGS(AS, BS, KS, FA, FB)                                                            \
   _Pragma("unroll") for (int ti = 0; ti < TI; ti++) FA[ti] = OA::frag(AS, wi * WTI + ti * 32, KS, lane); \
@@ -355,13 +371,13 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   // ST(ks): work interleaved with substep ks (the next tile's LDS stores)
 #define GEMM_COMPUTE_ST(AS, BS, CSV, PP, ST)                                                      \
   {                                                                                               \
-    F fa[2][TI], fb[2][TJ];                                                                       \
+    FI fa[2][TI], fb[2][TJ];                                                                      \
     if constexpr (PP) { GEMM_FRAGS(AS, BS, 0, fa[0], fb[0]) }                                     \
-    _Pragma("unroll") for (int ks = 0; ks < BK / 16; ks++) {                                      \
+    _Pragma("unroll") for (int ks = 0; ks < NSUB; ks++) {                                      \
       ST;                                                                                         \
       const int cur = PP ? ks & 1 : 0;                                                            \
       if constexpr (PP) {                                                                         \
-        if (ks + 1 < BK / 16) { GEMM_FRAGS(AS, BS, ks + 1, fa[cur ^ 1], fb[cur ^ 1]) }            \
+        if (ks + 1 < NSUB) { GEMM_FRAGS(AS, BS, ks + 1, fa[cur ^ 1], fb[cur ^ 1]) }            \
       } else {                                                                                    \
         GEMM_FRAGS(AS, BS, ks, fa[0], fb[0])                                                      \
       }                                                                                           \
@@ -402,8 +418,8 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
       b0.load(k2);                                                                                \
       if constexpr (ILV) {                                                                        \
         GEMM_COMPUTE_ST(sA[0], sB[0], CSV, PIPE,                                                  \
-                        (a1.template store_part<BK / 16>(sA[1], tid, ks),                         \
-                         b1.template store_part<BK / 16>(sB[1], tid, ks)))                        \
+                        (a1.template store_part<NSUB>(sA[1], tid, ks),                         \
+                         b1.template store_part<NSUB>(sB[1], tid, ks)))                        \
       } else {                                                                                    \
         GEMM_COMPUTE(sA[0], sB[0], CSV, PIPE)                                                     \
         a1.store(sA[1], tid);                                                                     \
@@ -415,8 +431,8 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
       b1.load(k3);                                                                                \
       if constexpr (ILV) {                                                                        \
         GEMM_COMPUTE_ST(sA[1], sB[1], CSV, PIPE,                                                  \
-                        (a0.template store_part<BK / 16>(sA[0], tid, ks),                         \
-                         b0.template store_part<BK / 16>(sB[0], tid, ks)))                        \
+                        (a0.template store_part<NSUB>(sA[0], tid, ks),                         \
+                         b0.template store_part<NSUB>(sB[0], tid, ks)))                        \
       } else {                                                                                    \
         GEMM_COMPUTE(sA[1], sB[1], CSV, PIPE)                                                     \
         a0.store(sA[0], tid);                                                                     \
@@ -551,6 +567,15 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   constexpr int BATCH = NBV > 1 ? NCH : EPI == EPI_RESID ? (NCH < 3 ? NCH : 3) : 1;
   static_assert(NBV == 1 || BATCH == NCH, "bias chunk index must be a constant");
   const bool use_bias = HAS_BIAS && (EPI != EPI_STORE || g.bias != nullptr);
+  // FP8 operands: the column scales of a thread's chunks (fixed columns, as the bias)
+  f32x8 sbv[FP8 ? NBV : 1];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int k = 0; k < NBV; k++) {
+      const int j = j0 + ((tid + k * NT) % CPRW) * 8;
+      sbv[k] = j < g.N ? ld8(g.scale_b + j) : f32x8{};
+    }
+  }
   f32x8 bv[NBV];
 #pragma unroll
   for (int k = 0; k < NBV; k++) {
@@ -601,6 +626,10 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
         const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl + 4);
         f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         const f32x8 bias = HOIST ? bv[NBV == 1 ? 0 : (b0 + k) % NBV] : (use_bias ? ld8(g.bias + j) : f32x8{});
+        if constexpr (FP8) {
+          static_assert(!FP8 || HOIST, "FP8 tiles keep their column scales in registers");
+          v *= sbv[NBV == 1 ? 0 : (b0 + k) % NBV] * g.scale_a[i];
+        }
         if constexpr (EPI == EPI_STORE || EPI == EPI_F32) v *= g.alpha;
         if constexpr (EPI == EPI_STORE) {
           if (use_bias) v += bias;
@@ -665,9 +694,9 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   }
 }
 
-template <typename T, int BM, int BN, int WI, int WJ, int AT, int BT, int EPI, int BK, int NBUF = 0>
+template <typename T, int BM, int BN, int WI, int WJ, int AT, int BT, int EPI, int BK, int NBUF = 0, typename TIn = T>
 hipError_t launch(hipStream_t st, const GemmArgs& g) {
-  constexpr int VE = Vec16<T>::n;
+  constexpr int VE = Vec16<TIn>::n;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.K <= 0 || g.splits < 1 || g.K % (g.splits * BK) != 0 || g.M % VE != 0 || g.N % 8 != 0 || g.lda % VE != 0 ||
       g.ldb % VE != 0 || (EPI != EPI_F32 && g.splits != 1) ||
@@ -675,7 +704,8 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
     return hipErrorInvalidValue;
   const int nbi = (g.M + BM - 1) / BM, nbj = (g.N + BN - 1) / BN;
   dim3 grid(nbi * nbj, g.splits);
-  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WI, WJ, AT, BT, EPI, NBUF>), grid, dim3(WI * WJ * 64), 0, st, g);
+  if (sizeof(TIn) == 1 && (g.scale_a == nullptr || g.scale_b == nullptr)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WI, WJ, AT, BT, EPI, NBUF, TIn>), grid, dim3(WI * WJ * 64), 0, st, g);
   return hipGetLastError();
 }
 
@@ -763,6 +793,20 @@ hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArg
   if ((k == TILE_256_W8 || k == TILE_256_W8_K32) && g.colsum)
     k = TILE_256x192_K32;  // the 8-wave tile has no bias-gradient path
   return p == BF16 ? dispatch<bf16>(st, a_t, b_t, epi, g, k) : dispatch<float>(st, a_t, b_t, epi, g, k);
+}
+
+hipError_t gemm_fp8(hipStream_t st, int epi, const GemmArgs& g) {
+  // forward products with FP8 E4M3 operands: the 8-wave tiles of the bf16
+  // path, BK = 128 (the same 128-byte LDS rows)
+  const bool w192 = g.N % 192 == 0 && g.N <= 2304;
+#define FP8_LAUNCH(E)                                                                                  \
+  return w192 ? launch<bf16, 256, 192, 4, 2, 0, 0, E, 128, 0, fp8e4>(st, g)                          \
+              : launch<bf16, 256, 256, 2, 4, 0, 0, E, 128, 0, fp8e4>(st, g);
+  if (epi == EPI_STORE) FP8_LAUNCH(EPI_STORE)
+  if (epi == EPI_GELU) FP8_LAUNCH(EPI_GELU)
+  if (epi == EPI_RESID) FP8_LAUNCH(EPI_RESID)
+#undef FP8_LAUNCH
+  return hipErrorInvalidValue;
 }
 
 int gemm_split_hint(Prec p, int a_t, int b_t, int M, int N, int K) {

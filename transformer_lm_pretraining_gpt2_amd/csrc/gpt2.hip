@@ -113,6 +113,10 @@ struct Plan {
   int64_t normpart;
   int64_t ska, sva, skb, svb, seg, nseg;
   int64_t flags, scale, norm;
+  // FP8 forward products: per-output-channel FP8 copy of the weights (laid out
+  // like the flat parameters) with its row scales, and one FP8 activation
+  // buffer with per-row scales shared by the forward's products
+  int64_t w8 = -1, wsc = -1, a8 = -1, asc = -1;
   std::vector<int> split;  // split-K factor per layer weight kind (qkv, proj, fc, fcproj)
 };
 
@@ -121,7 +125,8 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
   Plan P;
   const int64_t M = (int64_t)B * T, C = c.n_embd, L = c.n_layer, NH = c.n_head;
   const bool recompute = (prec & GPT2_RECOMPUTE_GELU) != 0;
-  prec &= ~GPT2_RECOMPUTE_GELU;
+  const bool fp8 = (prec & GPT2_FP8_FWD) != 0;
+  prec &= ~(GPT2_RECOMPUTE_GELU | GPT2_FP8_FWD);
   const int64_t a = prec == GPT2_BF16 ? 2 : 4;
   auto take = [&](int64_t bytes) {
     const int64_t off = P.bytes;
@@ -168,6 +173,12 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
     P.cspart[k] = take(4 * (int64_t)P.split[k] * wout[k]);
   }
   for (int k = 0; k < 3; k++) P.lnpart[k] = take(4 * (int64_t)layernorm_bwd_parts((int)M) * 2 * C);
+  if (fp8) {
+    P.w8 = take(make_layout(c).total);
+    P.wsc = take(4 * ((int64_t)c.padded_vocab_size + L * 9 * C));  // rows of wte and the four per-layer matrices
+    P.a8 = take(M * 4 * C);
+    P.asc = take(4 * M);
+  }
   P.normpart = take(8 * (int64_t)grad_norm_parts());
   P.ska = take(4 * M);
   P.sva = take(4 * M);
@@ -207,6 +218,9 @@ struct gpt2_handle {
   hipStream_t side = nullptr;
   bool overlap = true;
   bool recompute = false;  // GPT2_RECOMPUTE_GELU: the layers share one GELU-output buffer
+  bool fp8 = false;        // GPT2_FP8_FWD: forward products on FP8 copies
+  std::vector<QuantJob> wquant;     // the weights' FP8 copies, one job per matrix
+  std::vector<int64_t> wsc_off;     // [kind * (L+1) + layer+1]: row-scale offset (floats) in plan.wsc
   hipEvent_t ev_fork = nullptr, ev_done[4] = {nullptr, nullptr, nullptr, nullptr};
   Layout lay;
   Plan plan;
@@ -228,6 +242,13 @@ struct gpt2_handle {
                         : static_cast<const void*>(params + off);
   }
   int64_t act_bytes() const { return prec == BF16 ? 2 : 4; }
+  // FP8 copy of a weight matrix and its row scales
+  const unsigned char* W8(int kind, int layer = -1) {
+    return reinterpret_cast<const unsigned char*>(ws + plan.w8) + tensor(kind, layer).offset;
+  }
+  const float* WS(int kind, int layer = -1) {
+    return reinterpret_cast<const float*>(ws + plan.wsc) + wsc_off[kind * (cfg.n_layer + 1) + layer + 1];
+  }
 };
 
 namespace {
@@ -297,6 +318,29 @@ int run_gemm(gpt2_t* h, int kid, int a_t, int b_t, int epi, const GemmArgs& g, c
   hipError_t e = gemm(h->st, h->prec, a_t, b_t, epi, g);
   t.done();
   return hip_check(h, e, what);
+}
+
+// Forward matmul on FP8 copies: A = the shared FP8 activation buffer (rows
+// scaled by plan.asc), B = the weight's FP8 copy with its row scales.
+int run_gemm8(gpt2_t* h, int kid, int epi, GemmArgs g, int wkind, int layer, const char* what) {
+  g.A = h->w<unsigned char>(h->plan.a8);
+  g.scale_a = h->w<float>(h->plan.asc);
+  g.B = h->W8(wkind, layer);
+  g.scale_b = h->WS(wkind, layer);
+  Timer t(h, kid, 2.0 * g.M * g.N * g.K);
+  hipError_t e = gemm_fp8(h->st, epi, g);
+  t.done();
+  return hip_check(h, e, what);
+}
+
+// The weights' FP8 copies (after every update of the bf16 copy)
+int quantize_weights(gpt2_t* h) {
+  for (size_t i = 0; i < h->wquant.size(); i += kMaxQuantJobs) {
+    const int n = (int)std::min<size_t>(kMaxQuantJobs, h->wquant.size() - i);
+    int rc = hip_check(h, quant_jobs(h->st, h->wquant.data() + i, n), "weight fp8 copy");
+    if (rc) return rc;
+  }
+  return GPT2_OK;
 }
 
 // Forward-layer matmul: out = X W^T (+ epilogue); X [M, K] row-major, W [N, K].
@@ -471,8 +515,9 @@ int gpt2_check_shapes(const gpt2_config_t* cfg, int B, int T) {
 int64_t gpt2_workspace_bytes(const gpt2_config_t* cfg, int B, int T, int precision) {
   int rc = gpt2_check_shapes(cfg, B, T);
   if (rc) return rc;
-  const int base = precision & ~GPT2_RECOMPUTE_GELU;
+  const int base = precision & ~(GPT2_RECOMPUTE_GELU | GPT2_FP8_FWD);
   if (base != GPT2_FP32 && base != GPT2_BF16) return GPT2_ERR_ARG;
+  if ((precision & GPT2_FP8_FWD) && (base != GPT2_BF16 || cfg->n_embd % 256 != 0)) return GPT2_ERR_ARG;
   return make_plan(*cfg, B, T, precision).bytes;
 }
 
@@ -483,8 +528,10 @@ int gpt2_init(gpt2_t** out, const gpt2_config_t* cfg, int precision, int B, int 
   int rc = gpt2_check_shapes(cfg, B, T);
   if (rc) return rc;
   const bool recompute = (precision & GPT2_RECOMPUTE_GELU) != 0;
-  const int base = precision & ~GPT2_RECOMPUTE_GELU;
+  const bool fp8 = (precision & GPT2_FP8_FWD) != 0;
+  const int base = precision & ~(GPT2_RECOMPUTE_GELU | GPT2_FP8_FWD);
   if (base != GPT2_FP32 && base != GPT2_BF16) return GPT2_ERR_ARG;
+  if (fp8 && (base != GPT2_BF16 || cfg->n_embd % 256 != 0)) return GPT2_ERR_ARG;
   auto aligned = [](const void* p) { return p && (reinterpret_cast<uintptr_t>(p) % 256) == 0; };
   if (!aligned(params) || !aligned(grads) || !aligned(adam_m) || !aligned(adam_v) || !aligned(workspace))
     return GPT2_ERR_ARG;
@@ -496,6 +543,7 @@ int gpt2_init(gpt2_t** out, const gpt2_config_t* cfg, int precision, int B, int 
   h->cfg = *cfg;
   h->prec = base == GPT2_BF16 ? BF16 : F32;
   h->recompute = recompute;
+  h->fp8 = fp8;
   h->B = B;
   h->T = T;
   h->M = (int64_t)B * T;
@@ -510,6 +558,30 @@ int gpt2_init(gpt2_t** out, const gpt2_config_t* cfg, int precision, int B, int 
   h->plan = plan;
   h->by_kind_layer.assign(16 * (cfg->n_layer + 1), nullptr);
   for (auto& t : h->lay.t) h->by_kind_layer[t.kind * (cfg->n_layer + 1) + t.layer + 1] = &t;
+  if (fp8) {
+    // one quantization job per forward matrix, scales packed in plan.wsc
+    h->wsc_off.assign(16 * (cfg->n_layer + 1), -1);
+    int64_t rows = 0;
+    auto job = [&](int kind, int layer) {
+      const Tensor& t = h->tensor(kind, layer);
+      QuantJob q;
+      q.in = static_cast<const __bf16*>(params_lp) + t.offset;
+      q.out = reinterpret_cast<unsigned char*>(h->ws + plan.w8) + t.offset;
+      q.scale = reinterpret_cast<float*>(h->ws + plan.wsc) + rows;
+      q.rows = t.rows;
+      q.cols = t.cols;
+      h->wsc_off[kind * (cfg->n_layer + 1) + layer + 1] = rows;
+      rows += t.rows;
+      h->wquant.push_back(q);
+    };
+    job(T_WTE, -1);
+    for (int l = 0; l < cfg->n_layer; l++) {
+      job(T_QKVW, l);
+      job(T_PROJW, l);
+      job(T_FCW, l);
+      job(T_FCPW, l);
+    }
+  }
   // the deferred status flags live in the caller's workspace: start them at zero
   if (hipMemsetAsync(h->w<int>(plan.flags), 0, 16, h->st) != hipSuccess) {
     delete h;
@@ -560,7 +632,9 @@ int gpt2_set_overlap(gpt2_t* h, int enable) {
 int gpt2_refresh_params(gpt2_t* h) {
   if (!h) return GPT2_ERR_ARG;
   if (h->prec != BF16) return GPT2_OK;
-  return hip_check(h, to_bf16(h->st, h->params, h->params_lp, h->lay.total), "to_bf16");
+  int rc = hip_check(h, to_bf16(h->st, h->params, h->params_lp, h->lay.total), "to_bf16");
+  if (!rc && h->fp8) rc = quantize_weights(h);
+  return rc;
 }
 
 // The forward of training (train = 1: keeps what the backward needs, gelu'
@@ -576,6 +650,9 @@ static int forward_impl(gpt2_t* h, const int32_t* d_idx, const int32_t* d_target
   int rc;
   int* flags = h->w<int>(P.flags);
   h->have_fwd = false;
+  // FP8 forward products: the layer norms also write FP8 rows here
+  unsigned char* a8 = h->fp8 ? h->w<unsigned char>(P.a8) : nullptr;
+  float* asc = h->fp8 ? h->w<float>(P.asc) : nullptr;
 
   rc = hip_check(h, embed_fwd(h->st, d_idx, d_targets, h->P32(T_WTE), h->P32(T_WPE), h->w<float>(P.x_in[0]), h->B, h->T, C,
                               c.vocab_size, flags),
@@ -591,12 +668,15 @@ static int forward_impl(gpt2_t* h, const int32_t* d_idx, const int32_t* d_target
     {
       Timer t(h, K_LN_FWD, 0);
       rc = hip_check(h, layernorm_fwd(h->st, h->prec, h->w<float>(P.x_in[l]), h->P32(T_LN1G, l), h->P32(T_LN1B, l),
-                                      h->w<void>(P.h1[l]), h->w<float>(P.mean1[l]), h->w<float>(P.rstd1[l]), Mi, C),
+                                      h->w<void>(P.h1[l]), h->w<float>(P.mean1[l]), h->w<float>(P.rstd1[l]), Mi, C,
+                                      a8, asc),
                      "ln1");
     }
     if (rc) return rc;
     GemmArgs g = fwd_args(h, h->w<void>(P.h1[l]), h->W(T_QKVW, l), 3 * C, C, h->w<void>(P.qkv[l]), h->P32(T_QKVB, l));
-    if ((rc = run_gemm(h, K_GEMM_NT_STORE, 0, 0, EPI_STORE, g, "qkv"))) return rc;
+    if ((rc = h->fp8 ? run_gemm8(h, K_GEMM_NT_STORE, EPI_STORE, g, T_QKVW, l, "qkv")
+                     : run_gemm(h, K_GEMM_NT_STORE, 0, 0, EPI_STORE, g, "qkv")))
+      return rc;
     {
       const double pairs = (double)h->B * NH * ((double)h->T * (h->T + 1) / 2);
       Timer t(h, K_ATTN_FWD, 4.0 * hd * pairs);
@@ -605,14 +685,19 @@ static int forward_impl(gpt2_t* h, const int32_t* d_idx, const int32_t* d_target
                      "attn_fwd");
     }
     if (rc) return rc;
+    if (h->fp8 && (rc = hip_check(h, quant_rows(h->st, h->w<void>(P.atty[l]), a8, asc, Mi, C), "attn out fp8")))
+      return rc;
     g = fwd_args(h, h->w<void>(P.atty[l]), h->W(T_PROJW, l), C, C, h->w<void>(P.x_mid[l]), h->P32(T_PROJB, l));
     g.resid = h->w<float>(P.x_in[l]);
     g.ldr = C;
-    if ((rc = run_gemm(h, K_GEMM_NT_RESID, 0, 0, EPI_RESID, g, "proj"))) return rc;
+    if ((rc = h->fp8 ? run_gemm8(h, K_GEMM_NT_RESID, EPI_RESID, g, T_PROJW, l, "proj")
+                     : run_gemm(h, K_GEMM_NT_RESID, 0, 0, EPI_RESID, g, "proj")))
+      return rc;
     {
       Timer t(h, K_LN_FWD, 0);
       rc = hip_check(h, layernorm_fwd(h->st, h->prec, h->w<float>(P.x_mid[l]), h->P32(T_LN2G, l), h->P32(T_LN2B, l),
-                                      h->w<void>(P.h2[l]), h->w<float>(P.mean2[l]), h->w<float>(P.rstd2[l]), Mi, C),
+                                      h->w<void>(P.h2[l]), h->w<float>(P.mean2[l]), h->w<float>(P.rstd2[l]), Mi, C,
+                                      a8, asc),
                      "ln2");
     }
     if (rc) return rc;
@@ -620,22 +705,30 @@ static int forward_impl(gpt2_t* h, const int32_t* d_idx, const int32_t* d_target
     g.aux = train ? h->w<void>(P.u[l]) : nullptr;
     g.ldaux = 4 * C;
     g.preact = h->recompute;  // (in evaluation too, so its loss equals the training forward's)
-    if ((rc = run_gemm(h, K_GEMM_NT_GELU, 0, 0, EPI_GELU, g, "fc"))) return rc;
+    if ((rc = h->fp8 ? run_gemm8(h, K_GEMM_NT_GELU, EPI_GELU, g, T_FCW, l, "fc")
+                     : run_gemm(h, K_GEMM_NT_GELU, 0, 0, EPI_GELU, g, "fc")))
+      return rc;
+    if (h->fp8 && (rc = hip_check(h, quant_rows(h->st, h->w<void>(P.g[l]), a8, asc, Mi, 4 * C), "gelu out fp8")))
+      return rc;
     g = fwd_args(h, h->w<void>(P.g[l]), h->W(T_FCPW, l), C, 4 * C, h->w<void>(P.x_in[l + 1]), h->P32(T_FCPB, l));
     g.resid = h->w<float>(P.x_mid[l]);
     g.ldr = C;
-    if ((rc = run_gemm(h, K_GEMM_NT_RESID, 0, 0, EPI_RESID, g, "fcproj"))) return rc;
+    if ((rc = h->fp8 ? run_gemm8(h, K_GEMM_NT_RESID, EPI_RESID, g, T_FCPW, l, "fcproj")
+                     : run_gemm(h, K_GEMM_NT_RESID, 0, 0, EPI_RESID, g, "fcproj")))
+      return rc;
   }
   {
     Timer t(h, K_LN_FWD, 0);
     rc = hip_check(h, layernorm_fwd(h->st, h->prec, h->w<float>(P.x_in[L]), h->P32(T_LNFG), h->P32(T_LNFB),
-                                    h->w<void>(P.hf), h->w<float>(P.meanf), h->w<float>(P.rstdf), Mi, C),
+                                    h->w<void>(P.hf), h->w<float>(P.meanf), h->w<float>(P.rstdf), Mi, C, a8, asc),
                    "lnf");
   }
   if (rc) return rc;
   // tied output layer over the padded vocabulary
   GemmArgs g = fwd_args(h, h->w<void>(P.hf), h->W(T_WTE), c.padded_vocab_size, C, h->w<void>(P.logits), nullptr);
-  if ((rc = run_gemm(h, K_GEMM_NT_STORE, 0, 0, EPI_STORE, g, "lm_head"))) return rc;
+  if ((rc = h->fp8 ? run_gemm8(h, K_GEMM_NT_STORE, EPI_STORE, g, T_WTE, -1, "lm_head")
+                   : run_gemm(h, K_GEMM_NT_STORE, 0, 0, EPI_STORE, g, "lm_head")))
+    return rc;
   if (d_targets) {
     float* rows = d_loss_rows ? d_loss_rows : h->w<float>(P.loss_rows);
     {
@@ -800,6 +893,8 @@ int gpt2_adamw_step(gpt2_t* h, int step, float lr, float beta1, float beta2, flo
   rc = hip_check(h, adamw(h->st, h->params, h->grads, h->m, h->v, h->params_lp, h->lay.total, h->lay.n_decay, lr, beta1,
                           beta2, eps, weight_decay, (float)bc1, (float)bc2, scale, flags),
                  "adamw");
+  t.done();
+  if (!rc && h->fp8) rc = quantize_weights(h);
   return rc;
 }
 

@@ -37,6 +37,10 @@ struct GemmArgs {
   int64_t split_stride = 0;
   float alpha = 1.f;  // EPI_STORE / EPI_F32: acc is scaled by alpha before the bias / accumulation
   int preact = 0;     // EPI_GELU / EPI_GELU_BWD: aux holds the pre-activation (activation recompute)
+  // gemm_fp8: per-row scales of the FP8 operands, A(i, .) ~= A8(i, .) * scale_a[i]
+  // and B(j, .) ~= B8(j, .) * scale_b[j] (device [M] and [N])
+  const float* scale_a = nullptr;
+  const float* scale_b = nullptr;
   // EPI_F32 with a_t = 1 only: when set, the blocks of the first column tile also
   // write sum_r A(i, r) over their reduction range to colsum[split*colsum_stride + i]
   // (the bias gradient of a weight-gradient product, before the split reduction)
@@ -45,6 +49,9 @@ struct GemmArgs {
 };
 
 hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArgs& g);
+// forward product (a_t = b_t = 0) with FP8 E4M3 operands A, B (bytes) and
+// bf16 / fp32 outputs as in gemm; acc(i, j) is multiplied by scale_a[i] * scale_b[j]
+hipError_t gemm_fp8(hipStream_t st, int epi, const GemmArgs& g);
 // split-K factor that fills the chip for an M x N x K weight-gradient product
 int gemm_split_hint(Prec p, int a_t, int b_t, int M, int N, int K);
 
@@ -58,8 +65,10 @@ hipError_t attn_bwd_dkv(hipStream_t st, Prec p, const void* qkv, const void* dou
                         void* dqkv, int B, int T, int NH, int hd);
 
 // ---- LayerNorm ----
+// y8/s8 (optional, C a multiple of 256): FP8 E4M3 copy of the output rows with
+// one scale per row (y ~= y8 * s8[row])
 hipError_t layernorm_fwd(hipStream_t st, Prec p, const float* x, const float* g, const float* b, void* y, float* mean,
-                         float* rstd, int M, int C);
+                         float* rstd, int M, int C, unsigned char* y8 = nullptr, float* s8 = nullptr);
 // dres (+)= LN backward(dy); also writes dres_lp (act-type copy of dres) when p == BF16,
 // and per-block partials of dgamma/dbeta into part [nblk][2C].
 hipError_t layernorm_bwd(hipStream_t st, Prec p, const void* dy, const float* x, const float* mean, const float* rstd,
@@ -110,6 +119,23 @@ hipError_t adamw(hipStream_t st, float* p, const float* g, float* m, float* v, v
                  const int* skip);
 // bf16 copy of fp32 values
 hipError_t to_bf16(hipStream_t st, const float* src, void* dst, int64_t n);
+// FP8 E4M3 copies of bf16 rows with one scale per row (x ~= q * scale[row]):
+// scale = max|row| / 448, q = round(x / scale).  K a multiple of 8, <= 3072.
+hipError_t quant_rows(hipStream_t st, const void* x, unsigned char* q, float* scale, int rows, int K);
+constexpr int kMaxQuantJobs = 64;
+struct QuantJob {
+  const __bf16* in = nullptr;
+  unsigned char* out = nullptr;
+  float* scale = nullptr;
+  int rows = 0, cols = 0;
+  int row0 = 0;  // filled in by quant_jobs
+};
+struct QuantJobs {
+  QuantJob j[kMaxQuantJobs];
+  int count;
+};
+// several matrices in one launch (the weights' per-output-channel copies)
+hipError_t quant_jobs(hipStream_t st, const QuantJob* jobs, int count);
 // out = gelu_tanh(u) elementwise in the act type (n a multiple of 8)
 hipError_t gelu_fwd(hipStream_t st, Prec p, const void* u, void* out, int64_t n);
 

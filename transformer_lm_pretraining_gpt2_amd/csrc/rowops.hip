@@ -26,10 +26,21 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 // Lane l holds elements VE*l + 64*VE*k .. +VE-1 (k < C / (64*VE)): 16-byte
 // loads (VE = 4) when C is a multiple of 256, else VE = 2.
 // ---------------------------------------------------------------------------
+// FP8 E4M3 quantization of one row held by a wave: scale = amax / 448 (the
+// largest finite E4M3 value), q = round(v / scale) clamped to +-448 (the
+// conversion does not saturate).  A zero row gets scale 1.
+__device__ __forceinline__ float fp8_row_scale(float amax) { return amax > 0.f ? amax * (1.f / 448.f) : 1.f; }
+__device__ __forceinline__ unsigned fp8_pack4(float a, float b, float c, float d, float inv) {
+  auto cl = [](float t) { return fminf(fmaxf(t, -448.f), 448.f); };
+  unsigned p = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a * inv), cl(b * inv), 0, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(cl(c * inv), cl(d * inv), p, true);
+}
+
 template <typename T, int NP>
 __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* __restrict__ x, const float* __restrict__ g,
                                                      const float* __restrict__ b, T* __restrict__ y,
-                                                     float* __restrict__ mean, float* __restrict__ rstd, int M) {
+                                                     float* __restrict__ mean, float* __restrict__ rstd, int M,
+                                                     fp8e4* __restrict__ y8, float* __restrict__ s8) {
   constexpr int C = NP * 128;
   constexpr int VE = C % 256 == 0 ? 4 : 2, NC = C / (64 * VE);
   typedef float fv __attribute__((ext_vector_type(VE)));
@@ -57,6 +68,7 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* __restrict__ x
     }
   const float rs = 1.f / sqrtf(wave_sum(q) * (1.f / C) + 1e-5f);
   T* yr = y + (int64_t)row * C;
+  float amax = 0.f;
 #pragma unroll
   for (int k = 0; k < NC; k++) {
     const int c0 = VE * lane + 64 * VE * k;
@@ -64,8 +76,24 @@ __global__ void __launch_bounds__(256) ln_fwd_kernel(const float* __restrict__ x
     const fv bb = *reinterpret_cast<const fv*>(b + c0);
     tv o;
 #pragma unroll
-    for (int e = 0; e < VE; e++) o[e] = from_f<T>((v[k][e] - mu) * rs * gg[e] + bb[e]);
+    for (int e = 0; e < VE; e++) {
+      v[k][e] = (v[k][e] - mu) * rs * gg[e] + bb[e];
+      o[e] = from_f<T>(v[k][e]);
+      amax = fmaxf(amax, fabsf(v[k][e]));
+    }
     *reinterpret_cast<tv*>(yr + c0) = o;
+  }
+  if (y8) {  // FP8 copy of the output row with its own scale (forward products in FP8)
+    if constexpr (VE == 4) {
+      amax = wave_max(amax);
+      const float sc = fp8_row_scale(amax), inv = 1.f / sc;
+#pragma unroll
+      for (int k = 0; k < NC; k++) {
+        const int c0 = VE * lane + 64 * VE * k;
+        *reinterpret_cast<unsigned*>(y8 + (int64_t)row * C + c0) = fp8_pack4(v[k][0], v[k][1], v[k][2], v[k][3], inv);
+      }
+      if (lane == 0) s8[row] = sc;
+    }
   }
   if (lane == 0) {
     mean[row] = mu;
@@ -624,6 +652,58 @@ __global__ void __launch_bounds__(256) adamw_kernel(float* __restrict__ p, const
   }
 }
 
+// FP8 copy of bf16 rows [rows][K] with one scale per row; one wave per row,
+// the row kept in registers between the amax and the conversion.  CPL: 16-byte
+// chunks per lane (K <= 512 * CPL, K a multiple of 8).
+template <int CPL>
+__device__ __forceinline__ void quant_row(const bf16* __restrict__ xr, fp8e4* __restrict__ qr, float* __restrict__ sc,
+                                          int K, int lane) {
+  const int nch = K / 8;
+  bf16x8 v[CPL];
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; c++) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) {
+      v[c] = ld8(xr + ch * 8);
+#pragma unroll
+      for (int e = 0; e < 8; e++) amax = fmaxf(amax, fabsf((float)v[c][e]));
+    }
+  }
+  amax = wave_max(amax);
+  const float s = fp8_row_scale(amax), inv = 1.f / s;
+#pragma unroll
+  for (int c = 0; c < CPL; c++) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) {
+      uint2 o;
+      o.x = fp8_pack4((float)v[c][0], (float)v[c][1], (float)v[c][2], (float)v[c][3], inv);
+      o.y = fp8_pack4((float)v[c][4], (float)v[c][5], (float)v[c][6], (float)v[c][7], inv);
+      *reinterpret_cast<uint2*>(qr + ch * 8) = o;
+    }
+  }
+  if (lane == 0) *sc = s;
+}
+
+template <int CPL>
+__global__ void __launch_bounds__(256) quant_rows_kernel(const bf16* __restrict__ x, fp8e4* __restrict__ q,
+                                                         float* __restrict__ sc, int rows, int K) {
+  const int lane = threadIdx.x & 63, row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  quant_row<CPL>(x + (int64_t)row * K, q + (int64_t)row * K, sc + row, K, lane);
+}
+
+template <int CPL>
+__global__ void __launch_bounds__(256) quant_jobs_kernel(QuantJobs jobs) {
+  const int lane = threadIdx.x & 63, grow = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int j = 0;
+  while (j + 1 < jobs.count && grow >= jobs.j[j + 1].row0) j++;
+  const QuantJob& jb = jobs.j[j];
+  const int row = grow - jb.row0;
+  if (row < 0 || row >= jb.rows) return;
+  quant_row<CPL>(jb.in + (int64_t)row * jb.cols, jb.out + (int64_t)row * jb.cols, jb.scale + row, jb.cols, lane);
+}
+
 // gelu of a stored pre-activation (activation recompute): the same function of
 // the same rounded values as the forward's GELU epilogue, so the result is the
 // forward's activation bit for bit
@@ -663,14 +743,16 @@ __global__ void to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__
   }
 
 hipError_t layernorm_fwd(hipStream_t st, Prec p, const float* x, const float* g, const float* b, void* y, float* mean,
-                         float* rstd, int M, int C) {
-  if (C % 128 != 0) return hipErrorInvalidValue;
+                         float* rstd, int M, int C, fp8e4* y8, float* s8) {
+  if (C % 128 != 0 || (y8 && C % 256 != 0)) return hipErrorInvalidValue;
   dim3 grid((M + 3) / 4);
 #define LNF(NP)                                                                                                    \
   if (p == BF16)                                                                                                   \
-    hipLaunchKernelGGL((ln_fwd_kernel<bf16, NP>), grid, dim3(256), 0, st, x, g, b, static_cast<bf16*>(y), mean, rstd, M); \
+    hipLaunchKernelGGL((ln_fwd_kernel<bf16, NP>), grid, dim3(256), 0, st, x, g, b, static_cast<bf16*>(y), mean, rstd, M, \
+                       y8, s8);                                                                                    \
   else                                                                                                             \
-    hipLaunchKernelGGL((ln_fwd_kernel<float, NP>), grid, dim3(256), 0, st, x, g, b, static_cast<float*>(y), mean, rstd, M);
+    hipLaunchKernelGGL((ln_fwd_kernel<float, NP>), grid, dim3(256), 0, st, x, g, b, static_cast<float*>(y), mean, rstd, M, \
+                       y8, s8);
   LN_NP_DISPATCH(C, LNF)
 #undef LNF
   return hipGetLastError();
@@ -799,6 +881,39 @@ hipError_t adamw(hipStream_t st, float* p, const float* g, float* m, float* v, v
   const unsigned blocks = (unsigned)std::min<int64_t>((nq + 255) / 256, 1 << 30);
   hipLaunchKernelGGL(adamw_kernel, dim3(blocks), dim3(256), 0, st, p, g, m, v, static_cast<bf16*>(p_lp), nq, n_decay, lr,
                      b1, b2, eps, wd, 1.f / bc1, 1.f / bc2, scale, flags);
+  return hipGetLastError();
+}
+
+hipError_t quant_rows(hipStream_t st, const void* x, fp8e4* q, float* scale, int rows, int K) {
+  if (K % 8 != 0 || K > 512 * 6) return hipErrorInvalidValue;
+  const dim3 grid((rows + 3) / 4);
+  const bf16* xb = static_cast<const bf16*>(x);
+  if (K <= 512 * 2)
+    hipLaunchKernelGGL(quant_rows_kernel<2>, grid, dim3(256), 0, st, xb, q, scale, rows, K);
+  else
+    hipLaunchKernelGGL(quant_rows_kernel<6>, grid, dim3(256), 0, st, xb, q, scale, rows, K);
+  return hipGetLastError();
+}
+
+hipError_t quant_jobs(hipStream_t st, const QuantJob* jobs, int count) {
+  if (count <= 0) return hipSuccess;
+  if (count > kMaxQuantJobs) return hipErrorInvalidValue;
+  QuantJobs J;
+  J.count = count;
+  int rows = 0, kmax = 0;
+  for (int i = 0; i < count; i++) {
+    J.j[i] = jobs[i];
+    J.j[i].row0 = rows;
+    rows += jobs[i].rows;
+    kmax = std::max(kmax, jobs[i].cols);
+    if (jobs[i].cols % 8 != 0) return hipErrorInvalidValue;
+  }
+  if (kmax > 512 * 6) return hipErrorInvalidValue;
+  const dim3 grid((rows + 3) / 4);
+  if (kmax <= 512 * 2)
+    hipLaunchKernelGGL(quant_jobs_kernel<2>, grid, dim3(256), 0, st, J);
+  else
+    hipLaunchKernelGGL(quant_jobs_kernel<6>, grid, dim3(256), 0, st, J);
   return hipGetLastError();
 }
 
