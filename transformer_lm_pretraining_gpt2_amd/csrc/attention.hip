@@ -130,7 +130,14 @@ __global__ void __launch_bounds__(NW * 64, 3) attn_fwd_kernel(const T* __restric
   f32x16 o[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; dt++) o[dt] = f32x16{};
-  float m = -INFINITY, l = 0.f;  // running max and sum, log2 domain
+  // Running max m (log2 domain) and running sum: the sum is accumulated by
+  // the matrix core as (ones x P), so every entry of lsum holds this lane's
+  // query's sum of the very (rounded) P values that multiply V.
+  f32x16 lsum = f32x16{};
+  float m = -INFINITY;
+  F ones;
+#pragma unroll
+  for (int e = 0; e < 8; e++) ones[e] = from_f<T>(1.f);
   const int q = q0 + lr;
 
   const int ntiles = min(T_, (qblk + 1) * NW * WQ) / KT;
@@ -168,25 +175,27 @@ __global__ void __launch_bounds__(NW * 64, 3) attn_fwd_kernel(const T* __restric
 #pragma unroll
         for (int r = 0; r < 16; r++) mx = fmaxf(mx, s[c2][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2(m - mn);
-      float rs = 0.f;
+      // Lazy rescaling: the reference max moves only when this tile's max
+      // exceeds it by more than 8 (so P <= 2^8, exact in range for bf16 and
+      // fp32); then o and the sum are rescaled, in a branch the wave takes
+      // only if one of its queries needs it (the first tile, then rarely).
+      const bool grow = mx > m + 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mn = grow ? mx : m;
+        const float alpha = fast_exp2(m - mn);
+#pragma unroll
+        for (int dt = 0; dt < NDT; dt++) o[dt] *= alpha;
+        lsum *= alpha;
+        m = mn;
+      }
 #pragma unroll
       for (int c2 = 0; c2 < 2; c2++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const float p = fast_exp2(fmaf(s[c2][r], sl2, -mn));
-          s[c2][r] = p;
-          rs += p;
-        }
-      rs += __shfl_xor(rs, 32, 64);
-      l = l * alpha + rs;
-      m = mn;
-#pragma unroll
-      for (int dt = 0; dt < NDT; dt++) o[dt] *= alpha;
+        for (int r = 0; r < 16; r++) s[c2][r] = fast_exp2(fmaf(s[c2][r], sl2, -m));
 #pragma unroll
       for (int c = 0; c < KT / 16; c++) {
         const F pf = acc_frag<T>(s[c / 2], c % 2);
+        mma16(lsum, ones, pf);
 #pragma unroll
         for (int dt = 0; dt < NDT; dt++) mma16(o[dt], ld_tsplit<T, LD>(Vs[cur], dt * 32, c, lane), pf);
       }
@@ -198,6 +207,7 @@ __global__ void __launch_bounds__(NW * 64, 3) attn_fwd_kernel(const T* __restric
     __syncthreads();
   }
   if (!active) return;
+  const float l = lsum[0];
   const float inv = 1.f / l;
   T* orow = out + ((int64_t)b * T_ + q) * C + h * HD;
 #pragma unroll
