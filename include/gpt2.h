@@ -151,9 +151,10 @@ int gpt2_refresh_params(gpt2_t* h);
 int gpt2_set_stream(gpt2_t* h, void* stream);
 
 /* Overlap (default on): gpt2_backward runs each layer's four weight-gradient
- * products on a second stream owned by the handle (created by gpt2_init,
+ * products, and gpt2_forward the sort of the token ids for the embedding
+ * backward, on a second stream owned by the handle (created by gpt2_init,
  * default priority), ordered by events after their inputs and before anything
- * that overwrites those inputs; gpt2_backward returns with all of its work
+ * that overwrites those inputs; both calls return with all of their work
  * ordered before later work on the caller's stream, so the caller sees one
  * stream either way.  enable = 0 runs everything on the caller's stream
  * (same results, bit for bit; used to time kernels in isolation).

@@ -221,7 +221,9 @@ struct gpt2_handle {
   bool fp8 = false;        // GPT2_FP8_FWD: forward products on FP8 copies
   std::vector<QuantJob> wquant;     // the weights' FP8 copies, one job per matrix
   std::vector<int64_t> wsc_off;     // [kind * (L+1) + layer+1]: row-scale offset (floats) in plan.wsc
-  hipEvent_t ev_fork = nullptr, ev_done[4] = {nullptr, nullptr, nullptr, nullptr};
+  // ev_done[0..3]: a layer's weight-gradient products (qkv, proj, fc, fcproj)
+  // on the second stream; ev_done[4]: the forward's embedding sort there
+  hipEvent_t ev_fork = nullptr, ev_done[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
   Layout lay;
   Plan plan;
   std::vector<const Tensor*> by_kind_layer;  // [kind * (L+1) + layer+1]
@@ -659,9 +661,20 @@ static int forward_impl(gpt2_t* h, const int32_t* d_idx, const int32_t* d_target
                  "embed_fwd");
   if (rc) return rc;
   if (d_targets && train) {
-    rc = hip_check(h, embed_sort(h->st, d_idx, Mi, c.vocab_size, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva),
+    // the sort of the ids (for the embedding backward) needs only the ids: with
+    // overlap on it runs on the second stream beside the layers, joined back at
+    // the end of the forward
+    hipStream_t sst = h->st;
+    if (h->overlap) {
+      rc = hip_check(h, hipEventRecord(h->ev_fork, h->st), "fork");
+      if (!rc) rc = hip_check(h, hipStreamWaitEvent(h->side, h->ev_fork, 0), "fork wait");
+      if (rc) return rc;
+      sst = h->side;
+    }
+    rc = hip_check(h, embed_sort(sst, d_idx, Mi, c.vocab_size, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva),
                                  h->w<int32_t>(P.skb), h->w<int32_t>(P.svb), h->w<int32_t>(P.seg), h->w<int32_t>(P.nseg)),
                    "embed_sort");
+    if (!rc && h->overlap) rc = hip_check(h, hipEventRecord(h->ev_done[4], h->side), "sort done");
     if (rc) return rc;
   }
   for (int l = 0; l < L; l++) {
@@ -743,6 +756,10 @@ static int forward_impl(gpt2_t* h, const int32_t* d_idx, const int32_t* d_target
       rc = hip_check(h, mean_loss(h->st, rows, Mi, d_loss), "mean_loss");
       if (rc) return rc;
     }
+  }
+  if (d_targets && train && h->overlap) {
+    rc = hip_check(h, hipStreamWaitEvent(h->st, h->ev_done[4], 0), "sort join");
+    if (rc) return rc;
   }
   h->have_fwd = train;
   h->fwd_has_targets = d_targets != nullptr;
