@@ -222,8 +222,9 @@ struct gpt2_handle {
   std::vector<QuantJob> wquant;     // the weights' FP8 copies, one job per matrix
   std::vector<int64_t> wsc_off;     // [kind * (L+1) + layer+1]: row-scale offset (floats) in plan.wsc
   // ev_done[0..3]: a layer's weight-gradient products (qkv, proj, fc, fcproj)
-  // on the second stream; ev_done[4]: the forward's embedding sort there
-  hipEvent_t ev_fork = nullptr, ev_done[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  // on the second stream; ev_done[4]: the forward's embedding sort there;
+  // ev_done[5]: the tied head's weight gradient there
+  hipEvent_t ev_fork = nullptr, ev_done[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   Layout lay;
   Plan plan;
   std::vector<const Tensor*> by_kind_layer;  // [kind * (L+1) + layer+1]
@@ -791,11 +792,18 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
   float* dres = h->w<float>(P.dres);
   int rc;
 
-  // tied output layer: dhf = dlogits wte ; dwte (+)= dlogits^T hf   (both scaled by 1/K)
-  GemmArgs g = dx_args(h, h->w<void>(P.logits), h->W(T_WTE), Vp, C, h->w<void>(P.dh));
-  g.alpha = alpha;
-  if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "lm_head dx"))) return rc;
+  // tied output layer: dhf = dlogits wte ; dwte (+)= dlogits^T hf   (both scaled by 1/K).
+  // With overlap the weight gradient runs on the second stream beside the
+  // input gradient (both only read dlogits); the embedding backward, which
+  // adds the token rows' gradient into the same dwte, waits for it.
   {
+    hipStream_t main_st = h->st;
+    if (h->overlap) {
+      rc = hip_check(h, hipEventRecord(h->ev_fork, h->st), "fork");
+      if (!rc) rc = hip_check(h, hipStreamWaitEvent(h->side, h->ev_fork, 0), "fork wait");
+      if (rc) return rc;
+      h->st = h->side;
+    }
     GemmArgs w;
     w.A = h->w<void>(P.logits);
     w.lda = Vp;
@@ -808,8 +816,14 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     w.ldc = C;
     w.accumulate = acc;
     w.alpha = alpha;
-    if ((rc = run_gemm(h, K_GEMM_TN_LMHEAD, 1, 1, EPI_F32, w, "lm_head dw"))) return rc;
+    rc = run_gemm(h, K_GEMM_TN_LMHEAD, 1, 1, EPI_F32, w, "lm_head dw");
+    h->st = main_st;
+    if (!rc && h->overlap) rc = hip_check(h, hipEventRecord(h->ev_done[5], h->side), "join");
+    if (rc) return rc;
   }
+  GemmArgs g = dx_args(h, h->w<void>(P.logits), h->W(T_WTE), Vp, C, h->w<void>(P.dh));
+  g.alpha = alpha;
+  if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "lm_head dx"))) return rc;
   if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[L]), h->w<float>(P.meanf), h->w<float>(P.rstdf), T_LNFG,
                         -1, 0, 0, acc)))
     return rc;
@@ -885,6 +899,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     if ((rc = flush_reductions(h))) return rc;
   }
   if ((rc = flush_reductions(h))) return rc;
+  if ((rc = join_weight_grad(h, 5))) return rc;  // the tied head's weight gradient (second stream)
   // embeddings: position rows and the (tied) token rows, in a fixed order
   rc = hip_check(h, embed_bwd(h->st, dres, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva), h->w<int32_t>(P.seg),
                               h->w<int32_t>(P.nseg), h->G32(T_WTE), h->G32(T_WPE), h->w<float>(P.piece), h->B, h->T,
