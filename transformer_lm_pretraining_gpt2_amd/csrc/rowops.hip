@@ -458,12 +458,14 @@ __global__ void __launch_bounds__(64) dwte_run_kernel(const float* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Fused softmax cross-entropy, one block (1024 threads) per row, one pass over
-// the logits.  Each thread holds its share of the row, takes its own maximum
-// m_t and keeps e = exp(z - m_t) for its elements (one exponential per
-// logit); one block reduction combines the (m_t, sum e) pairs into
+// the logits in memory.  Each thread holds its share of the row in registers
+// as loaded (act type, so two rows fit per CU and one row's reductions overlap
+// another's memory traffic), takes its own maximum m_t and sum of
+// e = exp(z - m_t); one block reduction combines the (m_t, sum e) pairs into
 // logsumexp over the real vocabulary [0, V).  loss = logsumexp - z[target];
 // the logits are overwritten in place with dscale * (softmax - onehot), where
-// softmax = e * exp(m_t - logsumexp), and 0 on the padded columns.
+// softmax = exp(z - m_t) * exp(m_t - logsumexp) (the exponential taken again
+// from the held logits), and 0 on the padded columns.
 // ---------------------------------------------------------------------------
 constexpr int CE_T = 1024;
 
@@ -481,26 +483,23 @@ __global__ void __launch_bounds__(CE_T) ce_kernel(T* __restrict__ logits, const 
   const int y = min(max(tgt[row], 0), V - 1);  // out-of-range targets were flagged by the embedding pass
   if (tid == 0) zt = to_f<T>(z[y]);
   constexpr float L2E = 1.4426950408889634f;
-  // load this thread's vectors; columns >= V count as -inf
-  f32x8 e[NV];
+  // load this thread's vectors (held as loaded); columns >= V count as -inf
+  F zv[NV];
   float mt = -INFINITY;
+  auto val = [&](int k, int q) {
+    const int vi = tid + k * CE_T;
+    return vi * 8 + q < V ? to_f<T>(zv[k][q]) : -INFINITY;
+  };
 #pragma unroll
   for (int k = 0; k < NV; k++) {
     const int vi = tid + k * CE_T;
     if (vi < nvec) {
-      const F v = __builtin_nontemporal_load(reinterpret_cast<const F*>(z + vi * 8));
+      zv[k] = __builtin_nontemporal_load(reinterpret_cast<const F*>(z + vi * 8));
 #pragma unroll
-      for (int q = 0; q < 8; q++) e[k][q] = to_f<T>(v[q]);
-      if (vi * 8 + 8 > V) {
-#pragma unroll
-        for (int q = 0; q < 8; q++)
-          if (vi * 8 + q >= V) e[k][q] = -INFINITY;
-      }
-#pragma unroll
-      for (int q = 0; q < 8; q++) mt = fmaxf(mt, e[k][q]);
+      for (int q = 0; q < 8; q++) mt = fmaxf(mt, val(k, q));
     }
   }
-  // e = exp(z - m_t) and its sum (a thread without real columns keeps m_t = -inf, st = 0)
+  // sum of e = exp(z - m_t) (a thread without real columns keeps m_t = -inf, st = 0)
   float st = 0.f;
   const float mtl = mt == -INFINITY ? 0.f : mt * L2E;
 #pragma unroll
@@ -508,10 +507,7 @@ __global__ void __launch_bounds__(CE_T) ce_kernel(T* __restrict__ logits, const 
     const int vi = tid + k * CE_T;
     if (vi < nvec) {
 #pragma unroll
-      for (int q = 0; q < 8; q++) {
-        e[k][q] = __builtin_amdgcn_exp2f(fmaf(e[k][q], L2E, -mtl));
-        st += e[k][q];
-      }
+      for (int q = 0; q < 8; q++) st += __builtin_amdgcn_exp2f(fmaf(val(k, q), L2E, -mtl));
     }
   }
   // combine (m_t, st) over the block: M = max m_t, S = sum st * exp(m_t - M)
@@ -539,7 +535,7 @@ __global__ void __launch_bounds__(CE_T) ce_kernel(T* __restrict__ logits, const 
       F o;
 #pragma unroll
       for (int q = 0; q < 8; q++) {
-        float g = e[k][q] * f;
+        float g = __builtin_amdgcn_exp2f(fmaf(val(k, q), L2E, -mtl)) * f;
         if (vi * 8 + q == y) g -= dscale;
         o[q] = from_f<T>(g);
       }
