@@ -575,11 +575,24 @@ __global__ void __launch_bounds__(256) norm_part_kernel(const float* __restrict_
   const int64_t nq = n / 4;
   const int64_t per = (nq + gridDim.x - 1) / gridDim.x;
   const int64_t q0 = blockIdx.x * per, q1 = min(nq, q0 + per);
-  double s = 0.0;
-  for (int64_t q = q0 + tid; q < q1; q += 256) {
-    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + 4 * q));
-    s += (double)v[0] * v[0] + (double)v[1] * v[1] + (double)v[2] * v[2] + (double)v[3] * v[3];
+  // four loads in flight per thread, into four partial sums combined in a
+  // fixed order (the sum of squares is deterministic for a given n)
+  double s4[4] = {0.0, 0.0, 0.0, 0.0};
+  int64_t q = q0 + tid;
+  for (; q + 3 * 256 < q1; q += 4 * 256) {
+    f32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + 4 * (q + u * 256)));
+#pragma unroll
+    for (int u = 0; u < 4; u++)
+      s4[u] += (double)v[u][0] * v[u][0] + (double)v[u][1] * v[u][1] + (double)v[u][2] * v[u][2] +
+               (double)v[u][3] * v[u][3];
   }
+  for (; q < q1; q += 256) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g + 4 * q));
+    s4[0] += (double)v[0] * v[0] + (double)v[1] * v[1] + (double)v[2] * v[2] + (double)v[3] * v[3];
+  }
+  double s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   if (blockIdx.x == gridDim.x - 1)
     for (int64_t i = 4 * nq + tid; i < n; i += 256) s += (double)g[i] * g[i];
 #pragma unroll
