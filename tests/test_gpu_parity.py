@@ -267,3 +267,33 @@ def test_fp8_eval_equals_forward_and_narrow_width_is_rejected():
     assert le.item() == lf.item()
     with pytest.raises(RuntimeError):
         binding.TrainStep(PADDED, 2, 128, "bf16", fp8=True)  # width 128: the fused FP8 layer norm needs 256
+
+
+def test_fp8_with_recompute_and_accumulation():
+    # both flags together, two accumulated micro-steps (the weights' FP8 copies
+    # are rebuilt only by the update, so both micro-steps see the same copies)
+    lay = binding.param_layout(SMALL)
+    p0 = synth.init_params(lay, SMALL.n_layer, SMALL.vocab_size, dtype=np.float64)
+    big = batches(SMALL, 8, 256, 1, seed=123)[0]
+    micro = [(big[0][:4], big[1][:4]), (big[0][4:], big[1][4:])]
+    s = binding.TrainStep(SMALL, 4, 256, "bf16", fp8=True, recompute=True)
+    g = gpu_step(SMALL, 4, 256, "bf16", p0, micro, lr=1e-3, handle=s)
+    o = oracle_step(SMALL, p0, [big], lr=1e-3)
+    g["loss"] = [float(np.mean(g["loss"]))]
+    g["rows"] = [np.concatenate(g["rows"])]
+    compare(SMALL, g, o, "fp8")
+
+
+def test_recompute_eval_equals_forward():
+    import torch
+
+    s = binding.TrainStep(SMALL, 4, 256, "bf16", recompute=True)
+    s.set_params(synth.init_params(binding.param_layout(SMALL), SMALL.n_layer, SMALL.vocab_size))
+    (ids, tgt), = batches(SMALL, 4, 256, 1, seed=70)
+    d_ids = torch.from_numpy(ids.reshape(-1).astype(np.int32)).cuda()
+    d_tgt = torch.from_numpy(tgt.reshape(-1).astype(np.int32)).cuda()
+    le, lf = torch.zeros(1, device="cuda"), torch.zeros(1, device="cuda")
+    s.evaluate(d_ids, d_tgt, le)
+    s.forward(d_ids, d_tgt, lf)
+    assert s.sync_status() == 0
+    assert le.item() == lf.item()
