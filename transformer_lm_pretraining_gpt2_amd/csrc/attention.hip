@@ -20,6 +20,8 @@
 // k-operand: the 16 reduction slots of a (virtual) 32x32x16 MFMA may be any
 // 16 keys as long as both operands use the same assignment, here
 // key(c, g, s) = 16c + 8(s/4) + 4g + s%4 for chunk c, lane group g, slot s.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -99,7 +101,7 @@ __device__ __forceinline__ typename Frag<T>::type acc_frag(const f32x16& a, int 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ------------------------------------------------------------------------
-// Forward.  grid (ceil(T/128), NH, B); heavy (late) query blocks first.
+// Forward.  grid (NH*B, ceil(T/128)); heavy (late) query blocks first.
 // Per key tile: K and V rows (next tile prefetched into registers).
 // ------------------------------------------------------------------------
 template <typename T, int HD>
@@ -113,8 +115,8 @@ __global__ void __launch_bounds__(NW * 64, 3) attn_fwd_kernel(const T* __restric
   __shared__ __attribute__((aligned(16))) T Vs[2][KT * LD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), lr = lane & 31, lg = lane >> 5;
-  const int qblk = gridDim.x - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int qblk = gridDim.y - 1 - blockIdx.y;  // heaviest (latest) query blocks dispatch first
+  const int h = blockIdx.x % NH, b = blockIdx.x / NH;
   const int C = NH * HD, S3 = 3 * C;
   const int q0 = qblk * NW * WQ + w * WQ;
   const bool active = q0 < T_;
@@ -147,7 +149,11 @@ __global__ void __launch_bounds__(NW * 64, 3) attn_fwd_kernel(const T* __restric
   kt.store(Ks[0], tid);
   vt.store(Vs[0], tid);
   __syncthreads();
-  for (int it = 0; it < ntiles; it++) {
+  // One 64-key tile: prefetch the next tile, compute, stage the prefetch.
+  // Only the last two tiles can straddle one of the block's queries, so they
+  // run a copy with the causal mask and the rest a copy without it.
+  auto iteration = [&](int it, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
     const int cur = it & 1, kv0 = it * KT;
     const bool more = it + 1 < ntiles;
     if (more) {
@@ -162,12 +168,13 @@ __global__ void __launch_bounds__(NW * 64, 3) attn_fwd_kernel(const T* __restric
 #pragma unroll
         for (int ds = 0; ds < ND; ds++) mma16(s[c2], ld8(Ks[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), qf[ds]);
       }
-      if (kv0 + KT - 1 > q0) {  // diagonal tile: hide keys after the query
+      if (MASK) {  // hide keys after the query: key kl of the tile when kl > lim
+        const int lim = q - kv0 - 4 * lg;
 #pragma unroll
         for (int c2 = 0; c2 < 2; c2++)
 #pragma unroll
           for (int r = 0; r < 16; r++)
-            if (kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4) > q) s[c2][r] = -INFINITY;
+            if (c2 * 32 + 8 * (r / 4) + (r % 4) > lim) s[c2][r] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
@@ -205,7 +212,11 @@ __global__ void __launch_bounds__(NW * 64, 3) attn_fwd_kernel(const T* __restric
       vt.store(Vs[cur ^ 1], tid);
     }
     __syncthreads();
-  }
+  };
+  static_assert(NW * WQ == 2 * KT, "a block's queries span two key tiles");
+  const int nplain = max(0, ntiles - 2);
+  for (int it = 0; it < nplain; it++) iteration(it, std::false_type{});
+  for (int it = nplain; it < ntiles; it++) iteration(it, std::true_type{});
   if (!active) return;
   const float l = lsum[0];
   const float inv = 1.f / l;
@@ -223,7 +234,7 @@ __global__ void __launch_bounds__(NW * 64, 3) attn_fwd_kernel(const T* __restric
 }
 
 // ------------------------------------------------------------------------
-// dQ.  grid (ceil(T/128), NH, B).  Per query column (one per lane):
+// dQ.  grid (NH*B, ceil(T/128)), heavy blocks first.  Per query column (one per lane):
 // D = rowsum(dO * O) (stored for the dK/dV kernel, which runs after this one),
 // P^T = exp(S^T - LSE), dP^T = V dO^T, dS^T = P^T (dP^T - D), dQ = scale dS K.
 // Per key tile: K and V rows; K^T fragments come from transposing reads.
@@ -241,8 +252,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
   __shared__ __attribute__((aligned(16))) T Vs[2][KT * LD];
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), lr = lane & 31, lg = lane >> 5;
-  const int qblk = gridDim.x - 1 - blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int qblk = gridDim.y - 1 - blockIdx.y;  // heaviest (latest) query blocks dispatch first
+  const int h = blockIdx.x % NH, b = blockIdx.x / NH;
   const int C = NH * HD, S3 = 3 * C;
   const int q0 = qblk * NW * WQ + w * WQ;
   const bool active = q0 < T_;
@@ -281,7 +292,11 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
   kt.store(Ks[0], tid);
   vt.store(Vs[0], tid);
   __syncthreads();
-  for (int it = 0; it < ntiles; it++) {
+  // One 64-key tile: prefetch the next tile, compute, stage the prefetch.
+  // Only the last two tiles can straddle one of the block's queries, so they
+  // run a copy with the causal mask and the rest a copy without it.
+  auto iteration = [&](int it, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
     const int cur = it & 1, kv0 = it * KT;
     const bool more = it + 1 < ntiles;
     if (more) {
@@ -289,7 +304,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
       vt.load(vbase + (int64_t)(kv0 + KT) * S3, S3, tid);
     }
     if (active && kv0 <= q0 + WQ - 1) {
-      const bool diag = kv0 + KT - 1 > q0;
+      // key kl of the tile is masked for this lane's query when kl > lim
+      const int lim = q - kv0 - 4 * lg;
       // the tile's two 32-key halves one after the other: one S^T and one
       // dP^T accumulator live at a time
 #pragma unroll
@@ -301,11 +317,9 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
           mma16(dp, ld8(Vs[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), df[ds]);
         }
 #pragma unroll
-        for (int r = 0; r < 16; r++) s[r] = fast_exp2(fmaf(s[r], sl2, -lse2));
-        if (diag) {  // causal mask: only tiles that straddle this wave's queries
-#pragma unroll
-          for (int r = 0; r < 16; r++)
-            if (kv0 + c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4) > q) s[r] = 0.f;
+        for (int r = 0; r < 16; r++) {
+          s[r] = fast_exp2(fmaf(s[r], sl2, -lse2));
+          if (MASK && c2 * 32 + 8 * (r / 4) + (r % 4) > lim) s[r] = 0.f;
         }
 #pragma unroll
         for (int r = 0; r < 16; r++) s[r] = s[r] * (dp[r] - dq_d);  // dS^T
@@ -322,7 +336,11 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
       vt.store(Vs[cur ^ 1], tid);
     }
     __syncthreads();
-  }
+  };
+  static_assert(NW * WQ == 2 * KT, "a block's queries span two key tiles");
+  const int nplain = max(0, ntiles - 2);
+  for (int it = 0; it < nplain; it++) iteration(it, std::false_type{});
+  for (int it = nplain; it < ntiles; it++) iteration(it, std::true_type{});
   if (!active) return;
   T* row = dqkv + ((int64_t)b * T_ + q) * S3 + h * HD;
 #pragma unroll
@@ -337,7 +355,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
 }
 
 // ------------------------------------------------------------------------
-// dK, dV.  grid (ceil(T/128), NH, B); each wave owns 32 keys and walks the
+// dK, dV.  grid (NH*B, ceil(T/128)), heavy blocks first; each wave owns 32 keys and walks the
 // query tiles at or after them.  Per key column (one per lane):
 // P = exp(S - LSE), dV += dO^T P, dP = dO V^T, dS = P (dP - D), dK += scale Q^T dS.
 // Per query tile: Q and dO rows (their transposes come from transposing
@@ -357,8 +375,8 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
   __shared__ float Ls[2][KT], Dd[2][KT];
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), lr = lane & 31, lg = lane >> 5;
-  const int kblk = blockIdx.x;  // early key blocks see the most queries: they go first
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int kblk = blockIdx.y;  // early key blocks see the most queries: they dispatch first
+  const int h = blockIdx.x % NH, b = blockIdx.x / NH;
   const int C = NH * HD, S3 = 3 * C;
   const int k0 = kblk * NW * WQ + w * WQ;
   const bool active = k0 < T_;
@@ -402,7 +420,12 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
     Dd[0][tid] = sd;
   }
   __syncthreads();
-  for (int it = 0; it < ntiles; it++) {
+  // One 64-query tile: prefetch the next tile, compute, stage the prefetch.
+  // Only the first two tiles of a block can straddle one of its waves' keys,
+  // so they run a copy with the causal mask and the rest a copy without it,
+  // each one branch-free block the compiler schedules across both halves.
+  auto iteration = [&](int it, auto mask_c) {
+    constexpr bool MASK = decltype(mask_c)::value;
     const int cur = it & 1, qt0 = qt_begin + it * KT;
     const bool more = it + 1 < ntiles;
     if (more) {
@@ -414,39 +437,35 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
       }
     }
     if (active && qt0 + KT - 1 >= k0) {
-      const bool diag = qt0 < k0 + WQ - 1;
-      // the tile's two 32-query halves one after the other: only one S and
-      // one dP accumulator are live at a time
+      // query ql of the tile is masked for this lane's key when ql < lim
+      const int lim = kv - qt0 - 4 * lg;
+      // S and dP of both 32-query halves first, so the exponentials of the
+      // first half overlap the matrix products of the second
+      f32x16 s[2], dp[2];
 #pragma unroll
       for (int c2 = 0; c2 < 2; c2++) {
-        f32x16 s = f32x16{}, dp = f32x16{};
+        s[c2] = f32x16{};
+        dp[c2] = f32x16{};
 #pragma unroll
         for (int ds = 0; ds < ND; ds++) {
-          mma16(s, ld8(Qs[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), kf[ds]);
-          mma16(dp, ld8(Ds[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), vf[ds]);
+          mma16(s[c2], ld8(Qs[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), kf[ds]);
+          mma16(dp[c2], ld8(Ds[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), vf[ds]);
         }
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; c2++) {
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int ql = c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          s[r] = fast_exp2(fmaf(s[r], sl2, -Ls[cur][ql]));
-        }
-        if (diag) {  // causal mask: only tiles that straddle this wave's keys
-#pragma unroll
-          for (int r = 0; r < 16; r++) {
-            const int ql = c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-            if (qt0 + ql < kv) s[r] = 0.f;
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const int ql = c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          dp[r] = s[r] * (dp[r] - Dd[cur][ql]);
+          s[c2][r] = fast_exp2(fmaf(s[c2][r], sl2, -Ls[cur][ql]));
+          if (MASK && c2 * 32 + 8 * (r / 4) + (r % 4) < lim) s[c2][r] = 0.f;
+          dp[c2][r] = s[c2][r] * (dp[c2][r] - Dd[cur][ql]);
         }
 #pragma unroll
         for (int h2 = 0; h2 < 2; h2++) {
           const int c = 2 * c2 + h2;
-          const F pf = acc_frag<T>(s, h2);
-          const F sf = acc_frag<T>(dp, h2);
+          const F pf = acc_frag<T>(s[c2], h2);
+          const F sf = acc_frag<T>(dp[c2], h2);
 #pragma unroll
           for (int dt = 0; dt < NDT; dt++) {
             mma16(dv[dt], ld_tsplit<T, LD>(Ds[cur], dt * 32, c, lane), pf);
@@ -464,7 +483,11 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
       }
     }
     __syncthreads();
-  }
+  };
+  static_assert(NW * WQ == 2 * KT, "a block's keys span two query tiles");
+  const int nmask = min(2, ntiles);
+  for (int it = 0; it < nmask; it++) iteration(it, std::true_type{});
+  for (int it = nmask; it < ntiles; it++) iteration(it, std::false_type{});
   if (!active) return;
   T* row = dqkv + ((int64_t)b * T_ + kv) * S3 + h * HD;
 #pragma unroll
@@ -484,7 +507,9 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
 
 template <typename T, int HD>
 hipError_t fwd_t(hipStream_t st, const void* qkv, void* out, float* lse, int B, int T_, int NH) {
-  dim3 grid((T_ + NW * WQ - 1) / (NW * WQ), NH, B);
+  // blockIdx.x (dispatched fastest) walks the heads, blockIdx.y the row
+  // blocks from the most work to the least, so the long blocks start first
+  dim3 grid(NH * B, (T_ + NW * WQ - 1) / (NW * WQ));
   const float sl2 = LOG2E / sqrtf((float)HD);
   hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(qkv),
                      static_cast<T*>(out), lse, T_, NH, sl2);
@@ -494,7 +519,9 @@ hipError_t fwd_t(hipStream_t st, const void* qkv, void* out, float* lse, int B, 
 template <typename T, int HD>
 hipError_t dq_t(hipStream_t st, const void* qkv, const void* out, const void* dout, const float* lse, float* dsum,
                 void* dqkv, int B, int T_, int NH) {
-  dim3 grid((T_ + NW * WQ - 1) / (NW * WQ), NH, B);
+  // blockIdx.x (dispatched fastest) walks the heads, blockIdx.y the row
+  // blocks from the most work to the least, so the long blocks start first
+  dim3 grid(NH * B, (T_ + NW * WQ - 1) / (NW * WQ));
   const float scale = 1.f / sqrtf((float)HD), sl2 = LOG2E * scale;
   hipLaunchKernelGGL((attn_dq_kernel<T, HD>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(qkv),
                      static_cast<const T*>(out), static_cast<const T*>(dout), lse, dsum, static_cast<T*>(dqkv), T_, NH,
@@ -505,7 +532,9 @@ hipError_t dq_t(hipStream_t st, const void* qkv, const void* out, const void* do
 template <typename T, int HD>
 hipError_t dkv_t(hipStream_t st, const void* qkv, const void* dout, const float* lse, const float* dsum, void* dqkv,
                  int B, int T_, int NH) {
-  dim3 grid((T_ + NW * WQ - 1) / (NW * WQ), NH, B);
+  // blockIdx.x (dispatched fastest) walks the heads, blockIdx.y the row
+  // blocks from the most work to the least, so the long blocks start first
+  dim3 grid(NH * B, (T_ + NW * WQ - 1) / (NW * WQ));
   const float scale = 1.f / sqrtf((float)HD), sl2 = LOG2E * scale;
   hipLaunchKernelGGL((attn_dkv_kernel<T, HD>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(qkv),
                      static_cast<const T*>(dout), lse, dsum, static_cast<T*>(dqkv), T_, NH, sl2, scale);

@@ -274,8 +274,8 @@ struct Timer {
   Timer(gpt2_t* h_, int id, double flops) : h(h_), on(h_->timed == id) {
     if (on) {
       tl.flops = flops;
-      (void)hipEventCreate(&tl.a);
-      (void)hipEventCreate(&tl.b);
+      (void)hipEventCreateWithFlags(&tl.a, hipEventDisableSystemFence);
+      (void)hipEventCreateWithFlags(&tl.b, hipEventDisableSystemFence);
       (void)hipEventRecord(tl.a, h->st);
     }
   }
@@ -591,12 +591,12 @@ int gpt2_init(gpt2_t** out, const gpt2_config_t* cfg, int precision, int B, int 
     return GPT2_ERR_HIP;
   }
   if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
-      hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess) {
+      hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess) {
     gpt2_destroy(h);
     return GPT2_ERR_HIP;
   }
   for (auto& e : h->ev_done)
-    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess) {
       gpt2_destroy(h);
       return GPT2_ERR_HIP;
     }
