@@ -223,8 +223,9 @@ struct gpt2_handle {
   std::vector<int64_t> wsc_off;     // [kind * (L+1) + layer+1]: row-scale offset (floats) in plan.wsc
   // ev_done[0..3]: a layer's weight-gradient products (qkv, proj, fc, fcproj)
   // on the second stream; ev_done[4]: the forward's embedding sort there;
-  // ev_done[5]: the tied head's weight gradient there
-  hipEvent_t ev_fork = nullptr, ev_done[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  // ev_done[5]: the tied head's weight gradient there; ev_done[6]: a layer's
+  // batched reduction of partial sums there
+  hipEvent_t ev_fork = nullptr, ev_done[7] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   Layout lay;
   Plan plan;
   std::vector<const Tensor*> by_kind_layer;  // [kind * (L+1) + layer+1]
@@ -458,6 +459,23 @@ int side_weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, flo
 int join_weight_grad(gpt2_t* h, int wkind) {
   if (!h->overlap) return GPT2_OK;
   return hip_check(h, hipStreamWaitEvent(h->st, h->ev_done[wkind], 0), "join wait");
+}
+
+// The queued reductions of a layer on the side stream, after everything
+// enqueued so far on the main stream (the LayerNorm partials) and after the
+// layer's weight-gradient products (earlier on the same stream); signals
+// ev_done[6].  The main stream goes on with the next layer meanwhile.
+int side_flush_reductions(gpt2_t* h) {
+  if (!h->overlap) return flush_reductions(h);
+  int rc = hip_check(h, hipEventRecord(h->ev_fork, h->st), "fork");
+  if (!rc) rc = hip_check(h, hipStreamWaitEvent(h->side, h->ev_fork, 0), "fork wait");
+  if (rc) return rc;
+  hipStream_t main = h->st;
+  h->st = h->side;
+  rc = flush_reductions(h);
+  h->st = main;
+  if (!rc) rc = hip_check(h, hipEventRecord(h->ev_done[6], h->side), "flush done");
+  return rc;
 }
 
 int ln_backward(gpt2_t* h, const void* dy, const float* x, const float* mean, const float* rstd, int kind_g, int layer,
@@ -831,7 +849,8 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
   for (int l = L - 1; l >= 0; l--) {
     // activation recompute: rebuild this layer's GELU output in the shared
     // buffer (the last layer's is still there from the forward); the previous
-    // layer's readers of that buffer were joined before its reduction flush
+    // layer's reader of that buffer (its fcproj weight gradient) was joined
+    // before that layer's LayerNorm 2 backward
     if (h->recompute && l < L - 1) {
       rc = hip_check(h, gelu_fwd(h->st, h->prec, h->w<void>(P.u[l]), h->w<void>(P.g[l]), h->M * 4 * C), "gelu recompute");
       if (rc) return rc;
@@ -840,6 +859,8 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     if ((rc = side_weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), 3,
                                acc, "fcproj dw")))
       return rc;
+    // the next layer's MLP up-projection weight gradient read du
+    if (l < L - 1 && (rc = join_weight_grad(h, 2))) return rc;
     g = dx_args(h, dres_op, h->W(T_FCPW, l), C, 4 * C, h->w<void>(P.du));
     g.aux = h->w<void>(P.u[l]);
     g.ldaux = 4 * C;
@@ -862,7 +883,8 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
       return rc;
     g = dx_args(h, dres_op, h->W(T_PROJW, l), C, C, h->w<void>(P.datty));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "proj dx"))) return rc;
-    // attention
+    // attention (it rewrites dqkv, which the next layer's qkv weight gradient read)
+    if (l < L - 1 && (rc = join_weight_grad(h, 0))) return rc;
     {
       // dQ first: it also stores D = rowsum(dO * O), which dK/dV reads
       const double pairs = (double)h->B * NH * ((double)h->T * (h->T + 1) / 2);
@@ -893,12 +915,13 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[l]), h->w<float>(P.mean1[l]), h->w<float>(P.rstd1[l]),
                           T_LN1G, l, 2, 1, acc)))
       return rc;
-    // the layer's partial sums are complete once the last side-stream product
-    // (qkv) is; the next layer overwrites du and dqkv only after this point
-    if ((rc = join_weight_grad(h, 0))) return rc;
-    if ((rc = flush_reductions(h))) return rc;
+    // the layer's partial sums are reduced on the second stream behind its
+    // products; the LayerNorm partial buffers are rewritten by the next
+    // layer only after joins on later products of that stream
+    if ((rc = side_flush_reductions(h))) return rc;
   }
   if ((rc = flush_reductions(h))) return rc;
+  if ((rc = join_weight_grad(h, 6))) return rc;  // the last layer's reductions (second stream)
   if ((rc = join_weight_grad(h, 5))) return rc;  // the tied head's weight gradient (second stream)
   // embeddings: position rows and the (tied) token rows, in a fixed order
   rc = hip_check(h, embed_bwd(h->st, dres, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva), h->w<int32_t>(P.seg),
