@@ -290,7 +290,7 @@ __device__ __forceinline__ void dtl_schedule() {
 // (strided A, fp32 output) on 4-wave tiles.  The 8-wave tile serves only the
 // bias-free tied output layer; a second copy of its main loop would not fit
 // its 256 registers.
-constexpr bool gemm_has_colsum(int at, int epi, int waves) { return at == 1 && epi == EPI_F32 && waves == 4; }
+constexpr bool gemm_has_colsum(int at, int epi, int waves) { return at == 1 && epi == EPI_F32 && (waves == 4 || waves == 8); }
 
 // NBUF = 0: operands staged through registers (two register stages, two LDS
 // buffers).  NBUF >= 2 (bf16): direct-to-LDS loads into a ring of NBUF LDS
@@ -338,9 +338,12 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   const int bi = first_i + tig % gsize, bj = tig / gsize;
   const int i0 = bi * BM, j0 = bj * BN;
 
-  const int kchunk = g.K / g.splits;
-  const int kbeg = blockIdx.y * kchunk;
-  const int nk = kchunk / BK;
+  // split s of S takes reduction steps [s*nkt/S, (s+1)*nkt/S): the splits
+  // differ by at most one step, so any S fills the chip evenly
+  const int nkt = g.K / BK;
+  const int ks0 = (int)((int64_t)blockIdx.y * nkt / g.splits);
+  const int kbeg = ks0 * BK;
+  const int nk = (int)((int64_t)(blockIdx.y + 1) * nkt / g.splits) - ks0;
   const TIn* A = static_cast<const TIn*>(g.A);
   const TIn* Bm = static_cast<const TIn*>(g.B);
 
@@ -698,7 +701,8 @@ template <typename T, int BM, int BN, int WI, int WJ, int AT, int BT, int EPI, i
 hipError_t launch(hipStream_t st, const GemmArgs& g) {
   constexpr int VE = Vec16<TIn>::n;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  if (g.K <= 0 || g.splits < 1 || g.K % (g.splits * BK) != 0 || g.M % VE != 0 || g.N % 8 != 0 || g.lda % VE != 0 ||
+  if (g.K <= 0 || g.splits < 1 || g.K % BK != 0 || g.K / BK < g.splits || g.M % VE != 0 || g.N % 8 != 0 ||
+      g.lda % VE != 0 ||
       g.ldb % VE != 0 || (EPI != EPI_F32 && g.splits != 1) ||
       (g.colsum != nullptr && !gemm_has_colsum(AT, EPI, WI * WJ)))
     return hipErrorInvalidValue;
@@ -713,13 +717,13 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
 // from sweeps of the step's matmuls on MI355X.
 //  * 128x128, 4 waves of 64x64: two or three blocks per CU hide one block's
 //    prologue and epilogue behind the others' main loops; best for small
-//    products and short reductions.  With BK = 32 (41 KB of LDS, three
-//    blocks per CU) it is the weight-gradient tile.
+//    products and short reductions (and the fp32 path).
 //  * 8 waves, 256x256 (waves of 128x64, two per SIMD, twice the operand
 //    reuse): forward and input-gradient products with large outputs or long
 //    reductions (MLP up- and down-projection, tied head, input gradients of
-//    fc, qkv and the tied head); with BK = 32 the tied head's weight gradient.
-//  * 4 waves, 256x192, BK = 32: the smallest weight gradient.
+//    fc, qkv and the tied head); with BK = 32 every weight gradient (both
+//    operands reduction-strided), split over the reduction into as many
+//    uneven parts as make one round of one block per CU.
 //  * 8 waves, 256x192 (waves of 64x96), BK = 64: forward and input-gradient
 //    products whose output width is a multiple of 192 up to 2304 (the
 //    model-width outputs: 16384 x 768 makes 64 x 4 = 256 tiles, one per CU,
@@ -735,11 +739,7 @@ enum TileKind {
 TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
   if (p != BF16 || M < 256) return TILE_128;
   const int64_t mn = (int64_t)M * N;
-  if (a_t && b_t) {
-    if (mn >= 8000000) return TILE_256_W8_K32;
-    if (mn <= 1000000 && N % 192 == 0) return TILE_256x192_K32;
-    return TILE_128_K32;
-  }
+  if (a_t && b_t) return TILE_256_W8_K32;
   if (N % 192 == 0 && N <= 2304 && mn >= 4000000) return TILE_192_W8;
   if (K >= 2048 || mn >= 40000000) return (!a_t && !b_t && N <= 4096) ? TILE_D256_W8 : TILE_256_W8;
   return TILE_128;
@@ -789,9 +789,7 @@ hipError_t dispatch(hipStream_t st, int a_t, int b_t, int epi, const GemmArgs& g
 }  // namespace
 
 hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArgs& g) {
-  TileKind k = choose_tile(p, a_t, b_t, g.M, g.N, g.K);
-  if ((k == TILE_256_W8 || k == TILE_256_W8_K32) && g.colsum)
-    k = TILE_256x192_K32;  // the 8-wave tile has no bias-gradient path
+  const TileKind k = choose_tile(p, a_t, b_t, g.M, g.N, g.K);
   return p == BF16 ? dispatch<bf16>(st, a_t, b_t, epi, g, k) : dispatch<float>(st, a_t, b_t, epi, g, k);
 }
 
@@ -816,8 +814,13 @@ int gemm_split_hint(Prec p, int a_t, int b_t, int M, int N, int K) {
                  : (k == TILE_256_W8 || k == TILE_256_W8_K32 || k == TILE_D256_W8) ? 256 : 128;
   const int bk = tile_bk(p, k);
   const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
-  // one block per CU for the large tiles, two for 128x128; the reduction must
-  // split into equal multiples of the K step
+  if (a_t && b_t && k == TILE_256_W8_K32) {
+    // one round of one block per CU: as many splits as fit beside the tiles
+    // (uneven splits are allowed), each at least two reduction steps long
+    if (tiles >= 256) return 1;
+    return std::max(1, std::min(256 / tiles, K / bk / 2));
+  }
+  // one block per CU for the large tiles, two for 128x128; powers of two
   const int target = (k == TILE_128 || k == TILE_128_K32) ? 512 : 256;
   int s = 1;
   while (s < 16 && tiles * s < target && K % (2 * s * bk) == 0) s *= 2;
