@@ -311,7 +311,6 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   typedef Operand<TIn, BN, BK, NT, BT> OB;
   typedef typename Frag<TIn>::type FI;  // operand fragments
   typedef typename Frag<T>::type F;     // eight output values
-  typedef typename Quad<T>::type Q;
   // Operand tiles (two buffers each) and, after the main loop, the epilogue's
   // staging area for half of the output tile (fp32) share one LDS block.
   constexpr int RP = BM / WI;                 // output rows staged per pass (one row of waves)

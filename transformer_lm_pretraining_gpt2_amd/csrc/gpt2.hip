@@ -105,11 +105,14 @@ struct Plan {
   std::vector<int64_t> x_in, x_mid, h1, h2, mean1, rstd1, mean2, rstd2, qkv, atty, lse, u, g;
   int64_t hf, meanf, rstdf, logits, loss_rows, loss_tmp;
   int64_t dres, dres_lp, dh, datty, dqkv, du, dsum, piece;
+  // bf16: odd layers' du and dqkv, and LayerNorm 2's matmul copies of dres
+  // (even, odd layers); fp32: aliases of du, dqkv and dres
+  int64_t du2, dqkv2, lp2[2];
   // reduction partials, one buffer per producer so a whole layer's partial
   // sums can be reduced by one launch: weight kinds (qkv, proj, fc, fcproj)
   // for the split-K products and their bias column sums; LayerNorm slots
   // (final, ln_2, ln_1) for the gain/bias partials
-  int64_t wpart[4], cspart[4], lnpart[3];
+  int64_t wpart[4], cspart[4], lnpart[4];  // LayerNorm partials: final, LN2 (even, odd layers), LN1
   int64_t normpart;
   int64_t ska, sva, skb, svb, seg, nseg;
   int64_t flags, scale, norm;
@@ -161,6 +164,16 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
   P.datty = take(a * M * C);
   P.dqkv = take(a * M * 3 * C);
   P.du = take(a * M * 4 * C);
+  if (prec == GPT2_BF16) {
+    P.du2 = take(a * M * 4 * C);
+    P.dqkv2 = take(a * M * 3 * C);
+    P.lp2[0] = take(a * M * C);
+    P.lp2[1] = take(a * M * C);
+  } else {
+    P.du2 = P.du;
+    P.dqkv2 = P.dqkv;
+    P.lp2[0] = P.lp2[1] = P.dres;
+  }
   P.dsum = take(4 * M * NH);
   P.piece = take(4 * M * C);
   const Prec pr = prec == GPT2_BF16 ? BF16 : F32;
@@ -172,7 +185,7 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
     P.wpart[k] = P.split[k] > 1 ? take(4 * (int64_t)P.split[k] * wsz[k]) : 0;
     P.cspart[k] = take(4 * (int64_t)P.split[k] * wout[k]);
   }
-  for (int k = 0; k < 3; k++) P.lnpart[k] = take(4 * (int64_t)layernorm_bwd_parts((int)M) * 2 * C);
+  for (int k = 0; k < 4; k++) P.lnpart[k] = take(4 * (int64_t)layernorm_bwd_parts((int)M) * 2 * C);
   if (fp8) {
     P.w8 = take(make_layout(c).total);
     P.wsc = take(4 * ((int64_t)c.padded_vocab_size + L * 9 * C));  // rows of wte and the four per-layer matrices
@@ -439,51 +452,37 @@ int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* d
   return rc;
 }
 
-// A weight-gradient product on the side stream: it starts after everything
-// enqueued so far on the main stream and signals ev_done[wkind] when done.
-int side_weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* dW, float* db, int wkind,
-                     int accumulate, const char* what) {
-  if (!h->overlap) return weight_grad(h, dY, X, N, K, dW, db, wkind, accumulate, what);
-  int rc = hip_check(h, hipEventRecord(h->ev_fork, h->st), "fork");
-  if (!rc) rc = hip_check(h, hipStreamWaitEvent(h->side, h->ev_fork, 0), "fork wait");
-  if (rc) return rc;
-  hipStream_t main = h->st;
-  h->st = h->side;
-  rc = weight_grad(h, dY, X, N, K, dW, db, wkind, accumulate, what);
-  h->st = main;
-  if (!rc) rc = hip_check(h, hipEventRecord(h->ev_done[wkind], h->side), "join");
-  return rc;
-}
-
 // The main stream waits for the side-stream product of weight kind wkind.
 int join_weight_grad(gpt2_t* h, int wkind) {
   if (!h->overlap) return GPT2_OK;
   return hip_check(h, hipStreamWaitEvent(h->st, h->ev_done[wkind], 0), "join wait");
 }
 
-// The queued reductions of a layer on the side stream, after everything
-// enqueued so far on the main stream (the LayerNorm partials) and after the
-// layer's weight-gradient products (earlier on the same stream); signals
-// ev_done[6].  The main stream goes on with the next layer meanwhile.
-int side_flush_reductions(gpt2_t* h) {
-  if (!h->overlap) return flush_reductions(h);
+// Work enqueued between side_begin and side_end goes to the second stream,
+// after everything enqueued so far on the main stream; side_end records
+// ev_done[ev] there.  Without overlap both are no-ops (the main stream).
+int side_begin(gpt2_t* h, hipStream_t* saved) {
+  *saved = h->st;
+  if (!h->overlap) return GPT2_OK;
   int rc = hip_check(h, hipEventRecord(h->ev_fork, h->st), "fork");
   if (!rc) rc = hip_check(h, hipStreamWaitEvent(h->side, h->ev_fork, 0), "fork wait");
-  if (rc) return rc;
-  hipStream_t main = h->st;
-  h->st = h->side;
-  rc = flush_reductions(h);
-  h->st = main;
-  if (!rc) rc = hip_check(h, hipEventRecord(h->ev_done[6], h->side), "flush done");
+  if (!rc) h->st = h->side;
   return rc;
 }
 
+int side_end(gpt2_t* h, hipStream_t saved, int ev) {
+  h->st = saved;
+  if (!h->overlap) return GPT2_OK;
+  return hip_check(h, hipEventRecord(h->ev_done[ev], h->side), "side done");
+}
+
+// lp_off: workspace offset of the bf16 copy of dres it writes (bf16 only)
 int ln_backward(gpt2_t* h, const void* dy, const float* x, const float* mean, const float* rstd, int kind_g, int layer,
-                int slot, int accumulate_dres, int accumulate_grads) {
+                int slot, int64_t lp_off, int accumulate_dres, int accumulate_grads) {
   const int C = h->cfg.n_embd, M = (int)h->M;
   float* part = h->w<float>(h->plan.lnpart[slot]);
   int nparts = 0;
-  void* dres_lp = h->prec == BF16 ? h->w<void>(h->plan.dres_lp) : nullptr;
+  void* dres_lp = h->prec == BF16 ? h->w<void>(lp_off) : nullptr;
   Timer t(h, K_LN_BWD, 0);
   hipError_t e = layernorm_bwd(h->st, h->prec, dy, x, mean, rstd, h->P32(kind_g, layer), h->w<float>(h->plan.dres),
                                dres_lp, accumulate_dres, part, M, C, &nparts);
@@ -843,85 +842,109 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
   g.alpha = alpha;
   if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "lm_head dx"))) return rc;
   if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[L]), h->w<float>(P.meanf), h->w<float>(P.rstdf), T_LNFG,
-                        -1, 0, 0, acc)))
+                        -1, 0, P.dres_lp, 0, acc)))
     return rc;
 
+  // Second stream, per layer: one section before the MLP down-projection's
+  // input gradient (the previous layer's queued reductions, then this
+  // layer's fcproj weight gradient), one after it (fc), and one after the
+  // attention backward (proj, qkv).  The main stream joins it once per layer,
+  // before LayerNorm 1, which rewrites the matmul copy of dres that the fcproj
+  // weight gradient reads (and so, by stream order, after everything the
+  // second stream did for the layer above).  With bf16, du, dqkv and LayerNorm
+  // 2's copy of dres alternate between two buffers by layer, so their readers
+  // (two layers back) are covered by that join.  fp32 matmuls read dres itself,
+  // which every LayerNorm backward rewrites: there each rewrite waits for its
+  // readers, as does each single du / dqkv buffer.
+  const bool strict = !lp;
   for (int l = L - 1; l >= 0; l--) {
+    void* du = h->w<void>((l & 1) ? P.du2 : P.du);
+    void* dqkv = h->w<void>((l & 1) ? P.dqkv2 : P.dqkv);
+    const int64_t lp2_off = P.lp2[l & 1];
+    void* ln2_op = lp ? h->w<void>(lp2_off) : dres;  // matmul view of dres after LayerNorm 2
+    hipStream_t saved;
     // activation recompute: rebuild this layer's GELU output in the shared
-    // buffer (the last layer's is still there from the forward); the previous
-    // layer's reader of that buffer (its fcproj weight gradient) was joined
-    // before that layer's LayerNorm 2 backward
+    // buffer (the last layer's is still there from the forward); its reader
+    // in the layer above (the fcproj weight gradient) was joined before that
+    // layer's LayerNorm 1 backward
     if (h->recompute && l < L - 1) {
       rc = hip_check(h, gelu_fwd(h->st, h->prec, h->w<void>(P.u[l]), h->w<void>(P.g[l]), h->M * 4 * C), "gelu recompute");
       if (rc) return rc;
     }
     // MLP down-projection: dres is the gradient of the block output
-    if ((rc = side_weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), 3,
-                               acc, "fcproj dw")))
-      return rc;
-    // the next layer's MLP up-projection weight gradient read du
-    if (l < L - 1 && (rc = join_weight_grad(h, 2))) return rc;
-    g = dx_args(h, dres_op, h->W(T_FCPW, l), C, 4 * C, h->w<void>(P.du));
+    if ((rc = side_begin(h, &saved))) return rc;
+    rc = flush_reductions(h);  // the layer above's partial sums (and the final LayerNorm's)
+    if (!rc) rc = weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), 3, acc,
+                              "fcproj dw");
+    if (rc || (rc = side_end(h, saved, 3))) return rc;
+    if (strict && l < L - 1 && (rc = join_weight_grad(h, 2))) return rc;  // the layer above's fc weight gradient read du
+    g = dx_args(h, dres_op, h->W(T_FCPW, l), C, 4 * C, du);
     g.aux = h->w<void>(P.u[l]);
     g.ldaux = 4 * C;
     g.preact = h->recompute;
     if ((rc = run_gemm(h, K_GEMM_NN_GELU_BWD, 0, 1, EPI_GELU_BWD, g, "fcproj dx"))) return rc;
     // MLP up-projection
-    if ((rc = side_weight_grad(h, h->w<void>(P.du), h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), h->G32(T_FCB, l),
-                               2, acc, "fc dw")))
-      return rc;
-    g = dx_args(h, h->w<void>(P.du), h->W(T_FCW, l), 4 * C, C, h->w<void>(P.dh));
+    if ((rc = side_begin(h, &saved))) return rc;
+    rc = weight_grad(h, du, h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), h->G32(T_FCB, l), 2, acc, "fc dw");
+    if (rc || (rc = side_end(h, saved, 2))) return rc;
+    g = dx_args(h, du, h->W(T_FCW, l), 4 * C, C, h->w<void>(P.dh));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "fc dx"))) return rc;
-    // LayerNorm 2 rewrites the matmul copy of dres that the fcproj weight gradient reads
-    if ((rc = join_weight_grad(h, 3))) return rc;
+    if (strict && (rc = join_weight_grad(h, 3))) return rc;  // the fcproj weight gradient reads dres
     if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_mid[l]), h->w<float>(P.mean2[l]), h->w<float>(P.rstd2[l]),
-                          T_LN2G, l, 1, 1, acc)))
+                          T_LN2G, l, 1 + (l & 1), lp2_off, 1, acc)))
       return rc;
+    if (strict) {  // the projection's weight gradient now, before LayerNorm 1 rewrites dres
+      if ((rc = side_begin(h, &saved))) return rc;
+      rc = weight_grad(h, ln2_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l), 1, acc, "proj dw");
+      if (rc || (rc = side_end(h, saved, 1))) return rc;
+    }
     // attention output projection
-    if ((rc = side_weight_grad(h, dres_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l), 1,
-                               acc, "proj dw")))
-      return rc;
-    g = dx_args(h, dres_op, h->W(T_PROJW, l), C, C, h->w<void>(P.datty));
+    g = dx_args(h, ln2_op, h->W(T_PROJW, l), C, C, h->w<void>(P.datty));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "proj dx"))) return rc;
-    // attention (it rewrites dqkv, which the next layer's qkv weight gradient read)
-    if (l < L - 1 && (rc = join_weight_grad(h, 0))) return rc;
+    if (strict && l < L - 1 && (rc = join_weight_grad(h, 0))) return rc;  // the layer above's qkv weight gradient read dqkv
+    // attention
     {
       // dQ first: it also stores D = rowsum(dO * O), which dK/dV reads
       const double pairs = (double)h->B * NH * ((double)h->T * (h->T + 1) / 2);
       {
         Timer t(h, K_ATTN_DQ, 4.0 * hd * pairs);
         rc = hip_check(h, attn_bwd_dq(h->st, h->prec, h->w<void>(P.qkv[l]), h->w<void>(P.atty[l]), h->w<void>(P.datty),
-                                      h->w<float>(P.lse[l]), h->w<float>(P.dsum), h->w<void>(P.dqkv), h->B, h->T, NH,
-                                      hd),
+                                      h->w<float>(P.lse[l]), h->w<float>(P.dsum), dqkv, h->B, h->T, NH, hd),
                        "attn dq");
       }
       if (rc) return rc;
       {
         Timer t(h, K_ATTN_DKV, 4.0 * hd * pairs);
         rc = hip_check(h, attn_bwd_dkv(h->st, h->prec, h->w<void>(P.qkv[l]), h->w<void>(P.datty), h->w<float>(P.lse[l]),
-                                       h->w<float>(P.dsum), h->w<void>(P.dqkv), h->B, h->T, NH, hd),
+                                       h->w<float>(P.dsum), dqkv, h->B, h->T, NH, hd),
                        "attn dkv");
       }
       if (rc) return rc;
     }
-    // qkv projection
-    if ((rc = side_weight_grad(h, h->w<void>(P.dqkv), h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l),
-                               h->G32(T_QKVB, l), 0, acc, "qkv dw")))
-      return rc;
-    g = dx_args(h, h->w<void>(P.dqkv), h->W(T_QKVW, l), 3 * C, C, h->w<void>(P.dh));
+    // qkv projection (and, with bf16, the output projection's weight gradient)
+    if ((rc = side_begin(h, &saved))) return rc;
+    if (!strict)
+      rc = weight_grad(h, ln2_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l), 1, acc, "proj dw");
+    if (!rc) rc = weight_grad(h, dqkv, h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l), h->G32(T_QKVB, l), 0, acc,
+                              "qkv dw");
+    if (rc || (rc = side_end(h, saved, 0))) return rc;
+    g = dx_args(h, dqkv, h->W(T_QKVW, l), 3 * C, C, h->w<void>(P.dh));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "qkv dx"))) return rc;
-    // LayerNorm 1 rewrites the matmul copy of dres that the projection weight gradient reads
-    if ((rc = join_weight_grad(h, 1))) return rc;
+    // LayerNorm 1 rewrites the copy of dres the fcproj weight gradient read
+    // (fp32: dres itself, which the projection's weight gradient also reads)
+    if ((rc = join_weight_grad(h, strict ? 1 : 3))) return rc;
     if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[l]), h->w<float>(P.mean1[l]), h->w<float>(P.rstd1[l]),
-                          T_LN1G, l, 2, 1, acc)))
+                          T_LN1G, l, 3, P.dres_lp, 1, acc)))
       return rc;
-    // the layer's partial sums are reduced on the second stream behind its
-    // products; the LayerNorm partial buffers are rewritten by the next
-    // layer only after joins on later products of that stream
-    if ((rc = side_flush_reductions(h))) return rc;
   }
-  if ((rc = flush_reductions(h))) return rc;
-  if ((rc = join_weight_grad(h, 6))) return rc;  // the last layer's reductions (second stream)
+  // the last layer's partial sums, on the second stream behind its products
+  {
+    hipStream_t saved;
+    if ((rc = side_begin(h, &saved))) return rc;
+    rc = flush_reductions(h);
+    if (rc || (rc = side_end(h, saved, 6))) return rc;
+  }
+  if ((rc = join_weight_grad(h, 6))) return rc;  // everything on the second stream but the tied head
   if ((rc = join_weight_grad(h, 5))) return rc;  // the tied head's weight gradient (second stream)
   // embeddings: position rows and the (tied) token rows, in a fixed order
   rc = hip_check(h, embed_bwd(h->st, dres, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva), h->w<int32_t>(P.seg),
