@@ -79,8 +79,8 @@ def main(argv=None):
         name, t, avg = r["Name"], float(r["TotalDurationNs"]), float(r["AverageNs"])
         u = mf.get(name)
         util = (sum(u) / len(u)) / (avg * 1e-9) if u and avg > 0 else None
-        fb = [v for v in fetch.get(name, [])]
-        wb = [v for v in write.get(name, [])]
+        fb = [v for v, _ in fetch.get(name, [])]
+        wb = [v for v, _ in write.get(name, [])]
         gbs = None
         if fb and wb and avg > 0:
             bytes_ = (sum(fb) / len(fb)) * 1024 * fs + (sum(wb) / len(wb)) * 1024 * ws

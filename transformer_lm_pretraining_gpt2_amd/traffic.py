@@ -19,14 +19,16 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# kernel id -> mangled-name fragments of the instantiations it launches for
-# the GPT-2 124M bf16 workload (a launch of any of them counts as one launch)
+# kernel id -> (mangled-name fragments of the instantiations it launches for
+# the GPT-2 124M bf16 workload, most workgroups per launch or None); a launch
+# of any of them counts as one launch
 KERNELS = {
-    # weight gradients of the four per-layer linears: 128x128 tiles (qkv, fc,
-    # fcproj) and the 256x192 tile (attention projection), both BK = 32
-    "gemm_tn_f32": ["gemm_kernelIDF16bLi128ELi128ELi32ELi2ELi2ELi1ELi1ELi4E",
-                    "gemm_kernelIDF16bLi256ELi192ELi32ELi2ELi2ELi1ELi1ELi4E"],
-    "attn_bwd_dkv": ["attn_dkv_kernelIDF16bLi64E"],
+    # weight gradients of the four per-layer linears: the 8-wave 256x256 tile,
+    # BK = 32, split over the reduction into one round of at most one block
+    # per CU; the tied head's weight gradient (591 blocks) shares the
+    # instantiation and is left out by its size
+    "gemm_tn_f32": (["gemm_kernelIDF16bLi256ELi256ELi32ELi2ELi4ELi1ELi1ELi4E"], 256),
+    "attn_bwd_dkv": (["attn_dkv_kernelIDF16bLi64E"], None),
 }
 COPY = "copyBuffer"  # the runtime's device-to-device copy kernel, used by dst.copy_(src)
 
@@ -36,13 +38,16 @@ def read(path, counter):
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
-        out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        blocks = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+        out.setdefault(r["Kernel_Name"], []).append((float(r["Counter_Value"]), blocks))
         by_id[r["Dispatch_Id"]] = (r["Kernel_Name"], float(r["Counter_Value"]))
     return out, by_id
 
 
-def per_dispatch(rows, frags):
-    vals = [v for name, vs in rows.items() if any(f in name for f in frags) for v in vs]
+def per_dispatch(rows, spec):
+    frags, max_blocks = spec
+    vals = [v for name, vs in rows.items() if any(f in name for f in frags)
+            for v, blocks in vs if max_blocks is None or blocks <= max_blocks]
     if not vals:
         raise SystemExit(f"no dispatch matching {frags}")
     return sum(vals) / len(vals), len(vals)
