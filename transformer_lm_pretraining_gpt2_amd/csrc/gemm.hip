@@ -5,8 +5,8 @@
 // the tied output layer ("Karpathy's four-hour GPT-2 reproduction in one
 // post", part 1).  Either operand may be stored with the reduction index
 // contiguous (A(i, r) = A[i*lda + r]) or strided (A[r*lda + i]); strided
-// tiles are transposed in registers (8x8 blocks) on their way into LDS so the
-// MFMA fragments are always 16-byte LDS reads.
+// tiles keep their global layout in LDS and their MFMA fragments come from the
+// transposing LDS read.
 //
 // Block tile BM x BN, reduction step BK, double-buffered LDS with register
 // prefetch of the next tile; WI x WJ waves, each owning a (BM/WI) x (BN/WJ)
