@@ -566,7 +566,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   // the plain store and the fp32 partials, whose 8-wave kernels spill)
   // (and a thread with several bias chunks takes all its chunks at once, so
   // the bias array is indexed with constants)
-  constexpr int BATCH = NBV > 1 ? NCH : EPI == EPI_RESID ? (NCH < 3 ? NCH : 3) : 1;
+  constexpr int BATCH = NBV > 1 ? NCH : EPI == EPI_RESID ? (NCH < 3 ? NCH : 3) : EPI == EPI_GELU_BWD ? NCH : 1;
   static_assert(NBV == 1 || BATCH == NCH, "bias chunk index must be a constant");
   const bool use_bias = HAS_BIAS && (EPI != EPI_STORE || g.bias != nullptr);
   // FP8 operands: the column scales of a thread's chunks (fixed columns, as the bias)
@@ -587,6 +587,28 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   }
 #pragma unroll 1
   for (int pass = 0; pass < WI; pass++) {
+    // the row-dependent inputs (residual, gelu', accumulated partial) of a
+    // batch of chunks: the first batch's loads are issued before the staging
+    // barrier, so their latency overlaps the accumulators' trip through LDS
+    auto load_batch = [&](const int b0, f32x8 (&x)[BATCH], F (&u)[BATCH]) {
+#pragma unroll
+      for (int k = 0; k < BATCH; k++) {
+        const int c = tid + (b0 + k) * NT;
+        const int il = c / CPRW, jl = (c % CPRW) * 8;
+        const int i = i0 + pass * RP + il, j = j0 + jl;
+        if (b0 + k < NCH && c < RP * CPRW && i < g.M && j < g.N) {
+          if constexpr (EPI == EPI_RESID) x[k] = ld8(g.resid + (int64_t)i * g.ldr + j);
+          if constexpr (EPI == EPI_GELU_BWD) u[k] = ld8(static_cast<const T*>(g.aux) + (int64_t)i * g.ldaux + j);
+          if constexpr (EPI == EPI_F32) {
+            if (g.accumulate)
+              x[k] = ld8(static_cast<const float*>(g.C) + (int64_t)blockIdx.y * g.split_stride + (int64_t)i * g.ldc + j);
+          }
+        }
+      }
+    };
+    f32x8 x0[BATCH];
+    F u0[BATCH];
+    load_batch(0, x0, u0);
     __syncthreads();  // operand tiles (or the previous pass) are no longer read
     if (wi == pass) {
 #pragma unroll
@@ -604,19 +626,14 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
     auto chunk_batch = [&](const int b0) {
       f32x8 x[BATCH];
       F u[BATCH];
+      if (b0 == 0) {
 #pragma unroll
-      for (int k = 0; k < BATCH; k++) {
-        const int c = tid + (b0 + k) * NT;
-        const int il = c / CPRW, jl = (c % CPRW) * 8;
-        const int i = i0 + pass * RP + il, j = j0 + jl;
-        if (b0 + k < NCH && c < RP * CPRW && i < g.M && j < g.N) {
-          if constexpr (EPI == EPI_RESID) x[k] = ld8(g.resid + (int64_t)i * g.ldr + j);
-          if constexpr (EPI == EPI_GELU_BWD) u[k] = ld8(static_cast<const T*>(g.aux) + (int64_t)i * g.ldaux + j);
-          if constexpr (EPI == EPI_F32) {
-            if (g.accumulate)
-              x[k] = ld8(static_cast<const float*>(g.C) + (int64_t)blockIdx.y * g.split_stride + (int64_t)i * g.ldc + j);
-          }
+        for (int k = 0; k < BATCH; k++) {
+          x[k] = x0[k];
+          u[k] = u0[k];
         }
+      } else {
+        load_batch(b0, x, u);
       }
 #pragma unroll
       for (int k = 0; k < BATCH; k++) {
