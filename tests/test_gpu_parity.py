@@ -23,6 +23,10 @@ pytestmark = pytest.mark.gpu
 TINY = CONFIGS["tiny"].model
 PADDED = GPT2Config(vocab_size=509, padded_vocab_size=512, n_layer=2, n_head=4, n_embd=128, max_seq_len=128)
 SMALL = CONFIGS["small"].model
+# three layers of C = 384: odd layer count, and at 2048 tokens the bf16 weight
+# gradients split their 64 reduction steps into 25 (qkv), 32 (proj) and 21
+# (fc, fcproj) parts, uneven for three of the four
+MID = GPT2Config(vocab_size=509, padded_vocab_size=512, n_layer=3, n_head=6, n_embd=384, max_seq_len=512)
 
 
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
@@ -173,6 +177,26 @@ def test_overlapped_weight_gradients_match_serial():
     assert a["loss"] == b["loss"]
     for k in ("grads", "params", "m", "v"):
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_odd_layer_count_and_uneven_reduction_splits(prec):
+    # the backward alternates du, dqkv and LayerNorm 2's copy of dres between
+    # two buffers by layer parity and joins the second stream once per layer;
+    # with an odd layer count the last layer uses the odd buffers.  Against the
+    # oracle, and the overlapped schedule bit-identical to the serial one.
+    lay = binding.param_layout(MID)
+    p0 = synth.init_params(lay, MID.n_layer, MID.vocab_size, dtype=np.float64)
+    mb = batches(MID, 4, 512, 1, seed=77)
+    g = gpu_step(MID, 4, 512, prec, p0, mb)
+    o = oracle_step(MID, p0, mb)
+    compare(MID, g, o, prec)
+    s = binding.TrainStep(MID, 4, 512, prec)
+    s.set_overlap(False)
+    b = gpu_step(MID, 4, 512, prec, p0, mb, handle=s)
+    assert g["loss"] == b["loss"]
+    for k in ("grads", "params", "m", "v"):
+        assert np.array_equal(g[k], b[k]), k
 
 
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
