@@ -452,10 +452,11 @@ int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* d
   return rc;
 }
 
-// The main stream waits for the side-stream product of weight kind wkind.
-int join_weight_grad(gpt2_t* h, int wkind) {
+// The main stream waits for the second-stream work that recorded ev_done[ev]
+// (and, by that stream's order, for everything enqueued there before it).
+int join_side(gpt2_t* h, int ev) {
   if (!h->overlap) return GPT2_OK;
-  return hip_check(h, hipStreamWaitEvent(h->st, h->ev_done[wkind], 0), "join wait");
+  return hip_check(h, hipStreamWaitEvent(h->st, h->ev_done[ev], 0), "join wait");
 }
 
 // Work enqueued between side_begin and side_end goes to the second stream,
@@ -877,7 +878,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     if (!rc) rc = weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), 3, acc,
                               "fcproj dw");
     if (rc || (rc = side_end(h, saved, 3))) return rc;
-    if (strict && l < L - 1 && (rc = join_weight_grad(h, 2))) return rc;  // the layer above's fc weight gradient read du
+    if (strict && l < L - 1 && (rc = join_side(h, 2))) return rc;  // the layer above's fc weight gradient read du
     g = dx_args(h, dres_op, h->W(T_FCPW, l), C, 4 * C, du);
     g.aux = h->w<void>(P.u[l]);
     g.ldaux = 4 * C;
@@ -889,7 +890,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     if (rc || (rc = side_end(h, saved, 2))) return rc;
     g = dx_args(h, du, h->W(T_FCW, l), 4 * C, C, h->w<void>(P.dh));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "fc dx"))) return rc;
-    if (strict && (rc = join_weight_grad(h, 3))) return rc;  // the fcproj weight gradient reads dres
+    if (strict && (rc = join_side(h, 3))) return rc;  // the fcproj weight gradient reads dres
     if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_mid[l]), h->w<float>(P.mean2[l]), h->w<float>(P.rstd2[l]),
                           T_LN2G, l, 1 + (l & 1), lp2_off, 1, acc)))
       return rc;
@@ -901,7 +902,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     // attention output projection
     g = dx_args(h, ln2_op, h->W(T_PROJW, l), C, C, h->w<void>(P.datty));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "proj dx"))) return rc;
-    if (strict && l < L - 1 && (rc = join_weight_grad(h, 0))) return rc;  // the layer above's qkv weight gradient read dqkv
+    if (strict && l < L - 1 && (rc = join_side(h, 0))) return rc;  // the layer above's qkv weight gradient read dqkv
     // attention
     {
       // dQ first: it also stores D = rowsum(dO * O), which dK/dV reads
@@ -932,7 +933,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "qkv dx"))) return rc;
     // LayerNorm 1 rewrites the copy of dres the fcproj weight gradient read
     // (fp32: dres itself, which the projection's weight gradient also reads)
-    if ((rc = join_weight_grad(h, strict ? 1 : 3))) return rc;
+    if ((rc = join_side(h, strict ? 1 : 3))) return rc;
     if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[l]), h->w<float>(P.mean1[l]), h->w<float>(P.rstd1[l]),
                           T_LN1G, l, 3, P.dres_lp, 1, acc)))
       return rc;
@@ -944,8 +945,8 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     rc = flush_reductions(h);
     if (rc || (rc = side_end(h, saved, 6))) return rc;
   }
-  if ((rc = join_weight_grad(h, 6))) return rc;  // everything on the second stream but the tied head
-  if ((rc = join_weight_grad(h, 5))) return rc;  // the tied head's weight gradient (second stream)
+  if ((rc = join_side(h, 6))) return rc;  // everything on the second stream but the tied head
+  if ((rc = join_side(h, 5))) return rc;  // the tied head's weight gradient (second stream)
   // embeddings: position rows and the (tied) token rows, in a fixed order
   rc = hip_check(h, embed_bwd(h->st, dres, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva), h->w<int32_t>(P.seg),
                               h->w<int32_t>(P.nseg), h->G32(T_WTE), h->G32(T_WPE), h->w<float>(P.piece), h->B, h->T,
