@@ -180,6 +180,21 @@ def test_overlapped_weight_gradients_match_serial():
 
 
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_sequence_length_not_a_multiple_of_128(prec):
+    # T = 192: the attention kernels' second row block of 128 has only its
+    # first 64 rows, so half its waves are idle; the key blocks that start on
+    # the diagonal walk one (masked) query tile, and the dQ / forward blocks
+    # sweep a plain tile before the two masked ones
+    m = GPT2Config(vocab_size=509, padded_vocab_size=512, n_layer=2, n_head=4, n_embd=128, max_seq_len=192)
+    lay = binding.param_layout(m)
+    p0 = synth.random_params(lay, m.vocab_size, seed=21, scale=0.05)
+    mb = batches(m, 2, 192, 1, seed=23)
+    g = gpu_step(m, 2, 192, prec, p0, mb)
+    o = oracle_step(m, p0, mb)
+    compare(m, g, o, prec)
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
 def test_odd_layer_count_and_uneven_reduction_splits(prec):
     # the backward alternates du, dqkv and LayerNorm 2's copy of dres between
     # two buffers by layer parity and joins the second stream once per layer;
