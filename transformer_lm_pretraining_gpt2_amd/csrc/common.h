@@ -105,3 +105,11 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   if (nblocks % 8 != 0) return bid;
   return (bid % 8) * (nblocks / 8) + bid / 8;
 }
+
+// The same for any block count n = 8q + r: XCDs 0..r-1 take q + 1 logical
+// ids each, the others q (dispatched id bid goes to XCD bid % 8 as its
+// (bid / 8)-th block).
+__device__ __forceinline__ int xcd_remap_any(int bid, int nblocks) {
+  const int q = nblocks / 8, r = nblocks % 8, x = bid % 8;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + bid / 8;
+}

@@ -327,7 +327,18 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wi = wave / WJ, wj = wave % WJ;
   const int nbi = (g.M + BM - 1) / BM, nbj = (g.N + BN - 1) / BN;
-  const int tile = xcd_remap(blockIdx.x, nbi * nbj);
+  // With a split reduction each XCD takes a contiguous range of (split, tile)
+  // pairs in split-major order, so the token rows one split reads are fetched
+  // by one or two XCDs' L2 instead of all eight.
+  int tile, split = 0;
+  if (gridDim.y > 1) {
+    const int nt = nbi * nbj;
+    const int logical = xcd_remap_any(blockIdx.x + blockIdx.y * nt, nt * gridDim.y);
+    split = logical / nt;
+    tile = logical % nt;
+  } else {
+    tile = xcd_remap(blockIdx.x, nbi * nbj);
+  }
   // Grouped tile order: GM consecutive row-tiles sweep the columns together.
   constexpr int GM = 8;
   const int group = tile / (GM * nbj);
@@ -340,9 +351,9 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   // split s of S takes reduction steps [s*nkt/S, (s+1)*nkt/S): the splits
   // differ by at most one step, so any S fills the chip evenly
   const int nkt = g.K / BK;
-  const int ks0 = (int)((int64_t)blockIdx.y * nkt / g.splits);
+  const int ks0 = (int)((int64_t)split * nkt / g.splits);
   const int kbeg = ks0 * BK;
-  const int nk = (int)((int64_t)(blockIdx.y + 1) * nkt / g.splits) - ks0;
+  const int nk = (int)((int64_t)(split + 1) * nkt / g.splits) - ks0;
   const TIn* A = static_cast<const TIn*>(g.A);
   const TIn* Bm = static_cast<const TIn*>(g.B);
 
@@ -540,7 +551,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
     for (int ti = 0; ti < TI; ti++) {
       const float t = cs[ti] + __shfl_xor(cs[ti], 32, 64);  // the two halves of each row's reduction values
       const int i = i0 + wi * WTI + ti * 32 + (lane & 31);
-      if (lane < 32 && i < g.M) g.colsum[(int64_t)blockIdx.y * g.colsum_stride + i] = t;
+      if (lane < 32 && i < g.M) g.colsum[(int64_t)split * g.colsum_stride + i] = t;
     }
   }
   const int lr = lane & 31, lg = lane >> 5;
@@ -601,7 +612,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
           if constexpr (EPI == EPI_GELU_BWD) u[k] = ld8(static_cast<const T*>(g.aux) + (int64_t)i * g.ldaux + j);
           if constexpr (EPI == EPI_F32) {
             if (g.accumulate)
-              x[k] = ld8(static_cast<const float*>(g.C) + (int64_t)blockIdx.y * g.split_stride + (int64_t)i * g.ldc + j);
+              x[k] = ld8(static_cast<const float*>(g.C) + (int64_t)split * g.split_stride + (int64_t)i * g.ldc + j);
           }
         }
       }
@@ -697,7 +708,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
           }
           st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
         } else {  // EPI_F32
-          float* Cp = static_cast<float*>(g.C) + (int64_t)blockIdx.y * g.split_stride + (int64_t)i * g.ldc + j;
+          float* Cp = static_cast<float*>(g.C) + (int64_t)split * g.split_stride + (int64_t)i * g.ldc + j;
           if (g.accumulate) v += x[k];
           st8(Cp, v);
         }
