@@ -340,7 +340,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
     tile = xcd_remap(blockIdx.x, nbi * nbj);
   }
   // Grouped tile order: GM consecutive row-tiles sweep the columns together.
-  constexpr int GM = 8;
+  constexpr int GM = 4;
   const int group = tile / (GM * nbj);
   const int first_i = group * GM;
   const int gsize = min(nbi - first_i, GM);
