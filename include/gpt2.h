@@ -150,15 +150,15 @@ int gpt2_refresh_params(gpt2_t* h);
 /* Replaces the stream later calls enqueue on. */
 int gpt2_set_stream(gpt2_t* h, void* stream);
 
-/* Overlap (default on): gpt2_backward runs each layer's four weight-gradient
- * products, and gpt2_forward the sort of the token ids for the embedding
- * backward, on a second stream owned by the handle (created by gpt2_init,
- * default priority), ordered by events after their inputs and before anything
- * that overwrites those inputs; both calls return with all of their work
- * ordered before later work on the caller's stream, so the caller sees one
- * stream either way.  enable = 0 runs everything on the caller's stream
- * (same results, bit for bit; used to time kernels in isolation).
- * GPT2_ERR_ARG on a null handle. */
+/* Overlap (default on): gpt2_backward runs the tied head's and each layer's
+ * four weight-gradient products and the layers' partial-sum reductions, and
+ * gpt2_forward the sort of the token ids for the embedding backward, on a
+ * second stream owned by the handle (created by gpt2_init, default priority),
+ * ordered by events after their inputs and before anything that overwrites
+ * those inputs; both calls return with all of their work ordered before later
+ * work on the caller's stream, so the caller sees one stream either way.
+ * enable = 0 runs everything on the caller's stream (same results, bit for
+ * bit; used to time kernels in isolation).  GPT2_ERR_ARG on a null handle. */
 int gpt2_set_overlap(gpt2_t* h, int enable);
 
 /* ---- the step ---------------------------------------------------------------------- */
