@@ -847,7 +847,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     return rc;
 
   // Second stream, per layer: one section before the MLP down-projection's
-  // input gradient (the previous layer's queued reductions, then this
+  // input gradient (the layer above's queued reductions, then this
   // layer's fcproj weight gradient), one after it (fc), and one after the
   // attention backward (proj, qkv).  The main stream joins it once per layer,
   // before LayerNorm 1, which rewrites the matmul copy of dres that the fcproj
@@ -938,7 +938,8 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
                           T_LN1G, l, 3, P.dres_lp, 1, acc)))
       return rc;
   }
-  // the last layer's partial sums, on the second stream behind its products
+  // layer 0's partial sums (the last layer processed), on the second stream
+  // behind its products
   {
     hipStream_t saved;
     if ((rc = side_begin(h, &saved))) return rc;
