@@ -21,8 +21,12 @@
  * gpt2_last_error(h) gives a message for the last host-side failure.
  *
  * Shapes.  n_embd % n_head == 0, head_dim = n_embd / n_head in {32, 64},
- * n_embd % 128 == 0, padded_vocab_size % 128 == 0 and >= vocab_size,
- * vocab_size <= 2^24, T % 64 == 0 and T <= max_seq_len, B*T % 128 == 0.
+ * n_embd / 128 in {1, 2, 3, 4, 6, 8, 12, 16} (the LayerNorm row widths the
+ * library is built for), padded_vocab_size % 128 == 0, vocab_size <=
+ * padded_vocab_size <= 65536 (the cross-entropy row held by one block),
+ * T % 64 == 0 and T <= max_seq_len, B*T % 128 == 0.  A config outside these
+ * is refused by every call that takes one (GPT2_ERR_CONFIG), B or T outside
+ * them with GPT2_ERR_SHAPE, before any device work.
  */
 #ifndef GPT2_MI355X_H
 #define GPT2_MI355X_H
@@ -76,7 +80,9 @@ typedef enum { GPT2_FP32 = 0, GPT2_BF16 = 1 } gpt2_precision_t;
  * scale = max |row| / 448.  The backward stays bf16 (on the bf16 activations
  * and weights).  The workspace grows by the FP8 weight copy (one byte per
  * parameter), its row scales and one FP8 activation buffer of B*T*4*n_embd
- * bytes. */
+ * bytes.  Needs n_embd % 256 == 0 and n_embd <= 1024 (rows of at most 4096
+ * values are quantized); otherwise gpt2_workspace_bytes and gpt2_init return
+ * GPT2_ERR_ARG. */
 #define GPT2_FP8_FWD 0x200
 
 enum {
@@ -187,6 +193,18 @@ int gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, floa
  *   d_loss, d_loss_rows  as for gpt2_forward
  * Token-range errors as for gpt2_forward. */
 int gpt2_eval(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, float* d_loss, float* d_loss_rows);
+
+/* Device pointer to the fp32 residual stream [B*T, n_embd] (row-major, rows
+ * in [B][T] order) that the last gpt2_forward or gpt2_eval saved at the input
+ * of block `layer`: for 0 <= layer < n_layer the input of that block's first
+ * LayerNorm, for layer == n_layer the input of the final LayerNorm.  Layer 0
+ * is the embedding output x0[b, t] = wte[id[b, t]] + wpe[t] ("Karpathy's
+ * four-hour GPT-2 reproduction in one post", part 1: token plus position
+ * embedding), one fp32 addition per element.  The memory is part of the
+ * workspace: read-only for the caller, valid until the next forward on the
+ * handle, ordered on the handle's stream.  GPT2_ERR_ARG for a null handle or
+ * out pointer, or a layer outside [0, n_layer]. */
+int gpt2_residual(gpt2_t* h, int layer, const float** out);
 
 /* Backward pass of the last forward.  Adds (1/grad_accum_steps) times the
  * gradient of that micro-batch's mean loss into grads; micro_step == 0

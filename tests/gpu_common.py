@@ -94,9 +94,18 @@ def batches(model, B, T, K, seed, data="zipf", index0=0):
 # (measured 6 % at 4 layers, 8.6 % at 124M); the bar is 0.2, well below the
 # 100 % of a dropped scale or a transposed operand.  The loss moves by the
 # logits' perturbation (measured 2e-3 to 6e-3): bar 5e-2.
+# The per-position FP8 losses carry the logits' perturbation, which every
+# layer's four FP8 products feed with independent rounding noise: its RMS grows
+# as sqrt(n_layer), so the per-position bar is 0.2 at 12 layers, scaled by
+# sqrt(n_layer / 12) (0.28 for the 24-layer 350M model).
 TOL = {"fp32": dict(loss=1e-4, grad=1e-4, param=1e-4, rows=1e-4),
        "bf16": dict(loss=2e-2, grad=3e-2, param=3e-2, rows=1e-1),
        "fp8": dict(loss=5e-2, grad=2e-1, param=5e-2, rows=2e-1)}
+
+
+def rows_bar(model, prec):
+    bar = TOL[prec]["rows"]
+    return bar * (model.n_layer / 12) ** 0.5 if prec == "fp8" and model.n_layer > 12 else bar
 
 
 def compare(model, g, o, prec, check_rows=True):
@@ -106,8 +115,11 @@ def compare(model, g, o, prec, check_rows=True):
     for a, b in zip(g["loss"], o["loss"]):
         assert abs(a - b) <= tol["loss"], (a, b)
     if check_rows:
+        d = np.concatenate([np.abs(a - b) for a, b in zip(g["rows"], o["rows"])])
+        print(f"per-position loss diff: max {d.max():.3e}, rms {np.sqrt(np.mean(d * d)):.3e} "
+              f"(bar {rows_bar(model, prec):.3g})", flush=True)
         for a, b in zip(g["rows"], o["rows"]):
-            assert np.max(np.abs(a - b)) <= tol["rows"], np.max(np.abs(a - b))
+            assert np.max(np.abs(a - b)) <= rows_bar(model, prec), np.max(np.abs(a - b))
     lay = binding.param_layout(model)
     gv, ov = tensor_views(lay, g["grads"]), tensor_views(lay, o["grads"])
     worst = max((rel_l2(gv[n], ov[n]), n) for n in gv if np.linalg.norm(ov[n]) > 0)
@@ -121,6 +133,8 @@ def compare(model, g, o, prec, check_rows=True):
     wte_g = gv["wte"].reshape(model.padded_vocab_size, -1)
     assert np.all(wte_g[model.vocab_size:] == 0)
     assert abs(g["norm"] - o["norm"]) <= tol["grad"] * o["norm"]
+    print(f"params rel L2 {rel_l2(g['params'], o['params']):.3e}, norm rel diff "
+          f"{abs(g['norm'] - o['norm']) / o['norm']:.3e}", flush=True)
     assert rel_l2(g["params"], o["params"]) <= tol["param"]
     mv, ovm = tensor_views(lay, g["m"]), tensor_views(lay, o["m"])
     for n in mv:

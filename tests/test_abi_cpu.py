@@ -57,10 +57,24 @@ def test_workspace_and_shape_checks():
            GPT2Config(50257, 50176, 12, 12, 768, 1024),  # Vp < V
            GPT2Config(512, 512, 2, 3, 128, 64),  # C % nh
            GPT2Config(512, 512, 2, 1, 128, 64),  # head_dim 128
-           GPT2Config(512, 512, 2, 2, 96, 64)]  # C % 128
+           GPT2Config(512, 512, 2, 2, 96, 64),  # C % 128
+           # widths the LayerNorm kernels are not built for (C / 128 = 5, 7, 9, 10, 24)
+           GPT2Config(512, 512, 2, 10, 640, 64),
+           GPT2Config(512, 512, 2, 14, 896, 64),
+           GPT2Config(512, 512, 2, 18, 1152, 64),
+           GPT2Config(512, 512, 2, 20, 1280, 64),
+           GPT2Config(512, 512, 2, 48, 3072, 64),
+           # vocabularies wider than the cross-entropy row one block holds (65536)
+           GPT2Config(128256, 128256, 2, 12, 768, 64),
+           GPT2Config(100000, 100096, 2, 10, 640, 64),
+           GPT2Config(65537, 65664, 2, 12, 768, 64)]
     for c in bad:
-        assert binding.num_params(c) == -1
-        assert binding.check_shapes(c, 4, 64) == -1
+        assert binding.num_params(c) == -1, c
+        assert binding.check_shapes(c, 4, 64) == -1, c
+        assert binding.workspace_bytes(c, 4, 64, binding.GPT2_BF16) == -1, c
+    # every width the kernels are built for, and the widest vocabulary, pass
+    for k in (1, 2, 3, 4, 6, 8, 12, 16):
+        assert binding.check_shapes(GPT2Config(65536, 65536, 1, 2 * k, 128 * k, 64), 2, 64) == 0, k
 
 
 def test_init_rejects_bad_arguments_without_touching_the_device():
@@ -114,3 +128,24 @@ def test_fp8_flag_workspace():
     assert binding.workspace_bytes(m, B, T, binding.GPT2_FP32 | binding.GPT2_FP8_FWD) == -3
     narrow = GPT2Config(vocab_size=509, padded_vocab_size=512, n_layer=2, n_head=4, n_embd=128, max_seq_len=128)
     assert binding.workspace_bytes(narrow, 2, 128, binding.GPT2_BF16 | binding.GPT2_FP8_FWD) == -3
+    # GPT-2 350M (C = 1024, MLP rows of 4096 values) is the widest FP8 model the
+    # row quantizer holds; C = 1536 (rows of 6144) is refused at init
+    m350 = CONFIGS["gpt2_350m"].model
+    assert binding.workspace_bytes(m350, B, T, binding.GPT2_BF16 | binding.GPT2_FP8_FWD) > 0
+    wide = GPT2Config(vocab_size=50257, padded_vocab_size=50304, n_layer=2, n_head=24, n_embd=1536, max_seq_len=1024)
+    assert binding.check_shapes(wide, 16, 1024) == 0
+    assert binding.workspace_bytes(wide, 16, 1024, binding.GPT2_BF16) > 0
+    assert binding.workspace_bytes(wide, 16, 1024, binding.GPT2_BF16 | binding.GPT2_FP8_FWD) == -3
+    L = binding.lib()
+    c = binding.cconfig(wide)
+    h = ctypes.c_void_p()
+    fake = 1 << 20
+    ws = binding.workspace_bytes(wide, 16, 1024, binding.GPT2_BF16)
+    assert L.gpt2_init(ctypes.byref(h), ctypes.byref(c), binding.GPT2_BF16 | binding.GPT2_FP8_FWD, 16, 1024, fake, fake,
+                       fake, fake, fake, fake, 4 * ws, None) == -3
+
+
+def test_residual_accessor_rejects_bad_arguments():
+    L = binding.lib()
+    out = ctypes.c_void_p()
+    assert L.gpt2_residual(None, 0, ctypes.byref(out)) == -3

@@ -85,6 +85,34 @@ def test_grad_accumulation_matches_one_big_batch(prec):
     compare(PADDED, g, o, prec)
 
 
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_embedding_output_is_bit_exact(prec):
+    # x0[b, t] = wte[id[b, t]] + wpe[t]: one fp32 addition of the fp32 master
+    # rows, so the device's residual stream at block 0 equals numpy's sum bit
+    # for bit (both precisions gather from the fp32 masters).  Zipf ids put
+    # many positions on the same rows; V < Vp leaves padded rows unused.
+    import torch
+
+    lay = binding.param_layout(PADDED)
+    p0 = synth.random_params(lay, PADDED.vocab_size, seed=13, scale=0.05).astype(np.float32)
+    B, T = 4, 128
+    ids, tgt = batches(PADDED, B, T, 1, seed=31)[0]
+    s = binding.TrainStep(PADDED, B, T, prec)
+    s.set_params(p0)
+    s.forward(torch.from_numpy(ids.reshape(-1)).cuda(), torch.from_numpy(tgt.reshape(-1)).cuda())
+    assert s.sync_status() == 0
+    x0 = s.residual(0).cpu().numpy()
+    v = {e["name"]: e for e in lay}
+    C = PADDED.n_embd
+    wte = p0[:PADDED.padded_vocab_size * C].reshape(-1, C)
+    wpe = p0[v["wpe"]["offset"]:v["wpe"]["offset"] + PADDED.max_seq_len * C].reshape(-1, C)
+    want = (wte[ids.reshape(-1)] + np.tile(wpe[:T], (B, 1))).astype(np.float32)
+    assert x0.dtype == np.float32 and x0.shape == want.shape
+    assert np.array_equal(x0.view(np.uint32), want.view(np.uint32))
+    with pytest.raises(binding.Gpt2Error):
+        s.residual_ptr(PADDED.n_layer + 1)
+
+
 def test_step_is_deterministic():
     lay = binding.param_layout(SMALL)
     p0 = synth.init_params(lay, SMALL.n_layer, SMALL.vocab_size, dtype=np.float64)

@@ -51,6 +51,7 @@ SIGNATURES = [
     ("gpt2_set_overlap", _I, [_P, _I]),
     ("gpt2_forward", _I, [_P, _P, _P, _P, _P]),
     ("gpt2_eval", _I, [_P, _P, _P, _P, _P]),
+    ("gpt2_residual", _I, [_P, _I, ctypes.POINTER(_P)]),
     ("gpt2_backward", _I, [_P, _I, _I]),
     ("gpt2_adamw_step", _I, [_P, _I, _F, _F, _F, _F, _F, _F, _P]),
     ("gpt2_sync_status", _I, [_P]),
@@ -192,6 +193,22 @@ class TrainStep:
         """Forward-only loss (no backward state kept)."""
         p = lambda t: t.data_ptr() if t is not None else None
         self._check(lib().gpt2_eval(self.h, p(ids), p(targets), p(loss), p(loss_rows)), "eval")
+
+    def residual_ptr(self, layer):
+        """Device address of the fp32 residual stream [B*T, C] saved at the input
+        of block `layer` by the last forward (layer n_layer: the final LayerNorm's
+        input; layer 0: the embedding output)."""
+        ptr = ctypes.c_void_p()
+        self._check(lib().gpt2_residual(self.h, layer, ctypes.byref(ptr)), "residual")
+        return int(ptr.value)
+
+    def residual(self, layer):
+        """Copy of that residual stream as a float32 torch tensor [B*T, C] on the device."""
+        torch = self.torch
+        n = self.B * self.T * self.model.n_embd
+        off = self.residual_ptr(layer) - self.workspace.data_ptr()
+        assert 0 <= off and off + 4 * n <= self.workspace.numel()
+        return self.workspace[off:off + 4 * n].view(torch.float32).view(self.B * self.T, self.model.n_embd).clone()
 
     def backward(self, micro_step=0, grad_accum_steps=1):
         self._check(lib().gpt2_backward(self.h, micro_step, grad_accum_steps), "backward")

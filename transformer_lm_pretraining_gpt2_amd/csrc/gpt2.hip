@@ -78,15 +78,35 @@ Layout make_layout(const gpt2_config_t& c) {
   return L;
 }
 
+// Widths the row kernels are instantiated for: LayerNorm keeps a row in
+// registers as n_embd / 128 chunks per lane (1, 2, 3, 4, 6, 8, 12 or 16), and
+// the cross-entropy row as at most 8 vectors of 8 logits per thread of a
+// 1024-thread block (padded vocabulary <= 65536).
+bool ln_width_ok(int C) {
+  if (C <= 0 || C % 128 != 0) return false;
+  switch (C / 128) {
+    case 1: case 2: case 3: case 4: case 6: case 8: case 12: case 16: return true;
+    default: return false;
+  }
+}
+constexpr int kMaxPaddedVocab = 65536;
+
 int check_config(const gpt2_config_t* c) {
   if (!c) return GPT2_ERR_ARG;
-  if (c->vocab_size <= 0 || c->vocab_size > (1 << 24) || c->padded_vocab_size < c->vocab_size ||
+  if (c->vocab_size <= 0 || c->padded_vocab_size < c->vocab_size || c->padded_vocab_size > kMaxPaddedVocab ||
       c->padded_vocab_size % 128 != 0 || c->n_layer <= 0 || c->n_head <= 0 || c->n_embd <= 0 ||
-      c->n_embd % c->n_head != 0 || c->n_embd % 128 != 0 || c->n_embd > 2048 || c->max_seq_len <= 0)
+      c->n_embd % c->n_head != 0 || !ln_width_ok(c->n_embd) || c->max_seq_len <= 0)
     return GPT2_ERR_CONFIG;
   const int hd = c->n_embd / c->n_head;
   if (hd != 32 && hd != 64) return GPT2_ERR_CONFIG;
   return GPT2_OK;
+}
+
+// FP8 forward products: bf16 base precision; the LayerNorm's fused FP8 copy
+// needs a width that is a multiple of 256, and the row quantizer holds rows of
+// at most 4096 values (the MLP's 4 * n_embd), so n_embd <= 1024.
+bool fp8_ok(const gpt2_config_t* c, int base) {
+  return base == GPT2_BF16 && c->n_embd % 256 == 0 && 4 * c->n_embd <= 4096;
 }
 
 int check_bt(const gpt2_config_t* c, int B, int T) {
@@ -459,23 +479,34 @@ int join_side(gpt2_t* h, int ev) {
   return hip_check(h, hipStreamWaitEvent(h->st, h->ev_done[ev], 0), "join wait");
 }
 
-// Work enqueued between side_begin and side_end goes to the second stream,
-// after everything enqueued so far on the main stream; side_end records
-// ev_done[ev] there.  Without overlap both are no-ops (the main stream).
-int side_begin(gpt2_t* h, hipStream_t* saved) {
-  *saved = h->st;
-  if (!h->overlap) return GPT2_OK;
-  int rc = hip_check(h, hipEventRecord(h->ev_fork, h->st), "fork");
-  if (!rc) rc = hip_check(h, hipStreamWaitEvent(h->side, h->ev_fork, 0), "fork wait");
-  if (!rc) h->st = h->side;
-  return rc;
-}
+// Work enqueued while a SideSection is open goes to the second stream, after
+// everything enqueued so far on the main stream; close(ev) records ev_done[ev]
+// there.  Without overlap both are no-ops (the main stream).  The caller's
+// stream is put back when the section closes or goes out of scope, so an error
+// inside a section never leaves later calls enqueueing on the second stream.
+class SideSection {
+ public:
+  explicit SideSection(gpt2_t* h) : h_(h), saved_(h->st) {}
+  ~SideSection() { h_->st = saved_; }
+  SideSection(const SideSection&) = delete;
+  SideSection& operator=(const SideSection&) = delete;
+  int open() {
+    if (!h_->overlap) return GPT2_OK;
+    int rc = hip_check(h_, hipEventRecord(h_->ev_fork, h_->st), "fork");
+    if (!rc) rc = hip_check(h_, hipStreamWaitEvent(h_->side, h_->ev_fork, 0), "fork wait");
+    if (!rc) h_->st = h_->side;
+    return rc;
+  }
+  int close(int ev) {
+    h_->st = saved_;
+    if (!h_->overlap) return GPT2_OK;
+    return hip_check(h_, hipEventRecord(h_->ev_done[ev], h_->side), "side done");
+  }
 
-int side_end(gpt2_t* h, hipStream_t saved, int ev) {
-  h->st = saved;
-  if (!h->overlap) return GPT2_OK;
-  return hip_check(h, hipEventRecord(h->ev_done[ev], h->side), "side done");
-}
+ private:
+  gpt2_t* h_;
+  hipStream_t saved_;
+};
 
 // lp_off: workspace offset of the bf16 copy of dres it writes (bf16 only)
 int ln_backward(gpt2_t* h, const void* dy, const float* x, const float* mean, const float* rstd, int kind_g, int layer,
@@ -538,7 +569,7 @@ int64_t gpt2_workspace_bytes(const gpt2_config_t* cfg, int B, int T, int precisi
   if (rc) return rc;
   const int base = precision & ~(GPT2_RECOMPUTE_GELU | GPT2_FP8_FWD);
   if (base != GPT2_FP32 && base != GPT2_BF16) return GPT2_ERR_ARG;
-  if ((precision & GPT2_FP8_FWD) && (base != GPT2_BF16 || cfg->n_embd % 256 != 0)) return GPT2_ERR_ARG;
+  if ((precision & GPT2_FP8_FWD) && !fp8_ok(cfg, base)) return GPT2_ERR_ARG;
   return make_plan(*cfg, B, T, precision).bytes;
 }
 
@@ -552,7 +583,7 @@ int gpt2_init(gpt2_t** out, const gpt2_config_t* cfg, int precision, int B, int 
   const bool fp8 = (precision & GPT2_FP8_FWD) != 0;
   const int base = precision & ~(GPT2_RECOMPUTE_GELU | GPT2_FP8_FWD);
   if (base != GPT2_FP32 && base != GPT2_BF16) return GPT2_ERR_ARG;
-  if (fp8 && (base != GPT2_BF16 || cfg->n_embd % 256 != 0)) return GPT2_ERR_ARG;
+  if (fp8 && !fp8_ok(cfg, base)) return GPT2_ERR_ARG;
   auto aligned = [](const void* p) { return p && (reinterpret_cast<uintptr_t>(p) % 256) == 0; };
   if (!aligned(params) || !aligned(grads) || !aligned(adam_m) || !aligned(adam_v) || !aligned(workspace))
     return GPT2_ERR_ARG;
@@ -794,6 +825,13 @@ int gpt2_eval(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, float* 
   return forward_impl(h, d_idx, d_targets, d_loss, d_loss_rows, false);
 }
 
+int gpt2_residual(gpt2_t* h, int layer, const float** out) {
+  if (!h || !out) return GPT2_ERR_ARG;
+  if (layer < 0 || layer > h->cfg.n_layer) return fail(h, GPT2_ERR_ARG, "layer outside [0, n_layer]");
+  *out = h->w<float>(h->plan.x_in[layer]);
+  return GPT2_OK;
+}
+
 int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
   if (!h) return GPT2_ERR_ARG;
   if (grad_accum_steps < 1 || micro_step < 0 || micro_step >= grad_accum_steps)
@@ -863,7 +901,6 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     void* dqkv = h->w<void>((l & 1) ? P.dqkv2 : P.dqkv);
     const int64_t lp2_off = P.lp2[l & 1];
     void* ln2_op = lp ? h->w<void>(lp2_off) : dres;  // matmul view of dres after LayerNorm 2
-    hipStream_t saved;
     // activation recompute: rebuild this layer's GELU output in the shared
     // buffer (the last layer's is still there from the forward); its reader
     // in the layer above (the fcproj weight gradient) was joined before that
@@ -873,11 +910,14 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
       if (rc) return rc;
     }
     // MLP down-projection: dres is the gradient of the block output
-    if ((rc = side_begin(h, &saved))) return rc;
-    rc = flush_reductions(h);  // the layer above's partial sums (and the final LayerNorm's)
-    if (!rc) rc = weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), 3, acc,
-                              "fcproj dw");
-    if (rc || (rc = side_end(h, saved, 3))) return rc;
+    {
+      SideSection side(h);
+      if ((rc = side.open())) return rc;
+      rc = flush_reductions(h);  // the layer above's partial sums (and the final LayerNorm's)
+      if (!rc) rc = weight_grad(h, dres_op, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l), 3, acc,
+                                "fcproj dw");
+      if (rc || (rc = side.close(3))) return rc;
+    }
     if (strict && l < L - 1 && (rc = join_side(h, 2))) return rc;  // the layer above's fc weight gradient read du
     g = dx_args(h, dres_op, h->W(T_FCPW, l), C, 4 * C, du);
     g.aux = h->w<void>(P.u[l]);
@@ -885,9 +925,12 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     g.preact = h->recompute;
     if ((rc = run_gemm(h, K_GEMM_NN_GELU_BWD, 0, 1, EPI_GELU_BWD, g, "fcproj dx"))) return rc;
     // MLP up-projection
-    if ((rc = side_begin(h, &saved))) return rc;
-    rc = weight_grad(h, du, h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), h->G32(T_FCB, l), 2, acc, "fc dw");
-    if (rc || (rc = side_end(h, saved, 2))) return rc;
+    {
+      SideSection side(h);
+      if ((rc = side.open())) return rc;
+      rc = weight_grad(h, du, h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), h->G32(T_FCB, l), 2, acc, "fc dw");
+      if (rc || (rc = side.close(2))) return rc;
+    }
     g = dx_args(h, du, h->W(T_FCW, l), 4 * C, C, h->w<void>(P.dh));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "fc dx"))) return rc;
     if (strict && (rc = join_side(h, 3))) return rc;  // the fcproj weight gradient reads dres
@@ -895,9 +938,10 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
                           T_LN2G, l, 1 + (l & 1), lp2_off, 1, acc)))
       return rc;
     if (strict) {  // the projection's weight gradient now, before LayerNorm 1 rewrites dres
-      if ((rc = side_begin(h, &saved))) return rc;
+      SideSection side(h);
+      if ((rc = side.open())) return rc;
       rc = weight_grad(h, ln2_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l), 1, acc, "proj dw");
-      if (rc || (rc = side_end(h, saved, 1))) return rc;
+      if (rc || (rc = side.close(1))) return rc;
     }
     // attention output projection
     g = dx_args(h, ln2_op, h->W(T_PROJW, l), C, C, h->w<void>(P.datty));
@@ -923,12 +967,16 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
       if (rc) return rc;
     }
     // qkv projection (and, with bf16, the output projection's weight gradient)
-    if ((rc = side_begin(h, &saved))) return rc;
-    if (!strict)
-      rc = weight_grad(h, ln2_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l), 1, acc, "proj dw");
-    if (!rc) rc = weight_grad(h, dqkv, h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l), h->G32(T_QKVB, l), 0, acc,
-                              "qkv dw");
-    if (rc || (rc = side_end(h, saved, 0))) return rc;
+    {
+      SideSection side(h);
+      if ((rc = side.open())) return rc;
+      if (!strict)
+        rc = weight_grad(h, ln2_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l), 1, acc,
+                         "proj dw");
+      if (!rc) rc = weight_grad(h, dqkv, h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l), h->G32(T_QKVB, l), 0, acc,
+                                "qkv dw");
+      if (rc || (rc = side.close(0))) return rc;
+    }
     g = dx_args(h, dqkv, h->W(T_QKVW, l), 3 * C, C, h->w<void>(P.dh));
     if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "qkv dx"))) return rc;
     // LayerNorm 1 rewrites the copy of dres the fcproj weight gradient read
@@ -941,10 +989,10 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
   // layer 0's partial sums (the last layer processed), on the second stream
   // behind its products
   {
-    hipStream_t saved;
-    if ((rc = side_begin(h, &saved))) return rc;
+    SideSection side(h);
+    if ((rc = side.open())) return rc;
     rc = flush_reductions(h);
-    if (rc || (rc = side_end(h, saved, 6))) return rc;
+    if (rc || (rc = side.close(6))) return rc;
   }
   if ((rc = join_side(h, 6))) return rc;  // everything on the second stream but the tied head
   if ((rc = join_side(h, 5))) return rc;  // the tied head's weight gradient (second stream)

@@ -109,7 +109,10 @@ hipError_t cross_entropy(hipStream_t st, Prec p, void* logits, const int32_t* tg
 hipError_t mean_loss(hipStream_t st, const float* row_loss, int M, float* out);
 
 // ---- optimizer ----
-int grad_norm_parts();
+// fp64 partial sums of the gradient norm: one per block of the first pass,
+// every one written by each call (so a reused buffer needs no clearing)
+constexpr int kGradNormParts = 1024;
+inline int grad_norm_parts() { return kGradNormParts; }
 hipError_t grad_norm(hipStream_t st, const float* g, int64_t n, double* part, float clip, float* norm_out,
                      float* scale_out, int* err_flag);
 // AdamW over the flat buffer; indices < n_decay take weight decay.  g is
@@ -120,7 +123,7 @@ hipError_t adamw(hipStream_t st, float* p, const float* g, float* m, float* v, v
 // bf16 copy of fp32 values
 hipError_t to_bf16(hipStream_t st, const float* src, void* dst, int64_t n);
 // FP8 E4M3 copies of bf16 rows with one scale per row (x ~= q * scale[row]):
-// scale = max|row| / 448, q = round(x / scale).  K a multiple of 8, <= 3072.
+// scale = max|row| / 448, q = round(x / scale).  K a multiple of 8, <= 4096.
 hipError_t quant_rows(hipStream_t st, const void* x, unsigned char* q, float* scale, int rows, int K);
 constexpr int kMaxQuantJobs = 64;
 struct QuantJob {

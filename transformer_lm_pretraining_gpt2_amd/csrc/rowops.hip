@@ -566,7 +566,7 @@ __global__ void __launch_bounds__(1024) mean_loss_kernel(const float* __restrict
 // order), then one block adds the partials in order and derives the clip
 // factor min(1, clip / norm); a non-finite norm sets the error and skip flags.
 // ---------------------------------------------------------------------------
-constexpr int NORM_BLOCKS = 1024;
+constexpr int NORM_BLOCKS = kGradNormParts;
 
 __global__ void __launch_bounds__(256) norm_part_kernel(const float* __restrict__ g, int64_t n,
                                                         double* __restrict__ part) {
@@ -873,8 +873,6 @@ hipError_t mean_loss(hipStream_t st, const float* row_loss, int M, float* out) {
   return hipGetLastError();
 }
 
-int grad_norm_parts() { return NORM_BLOCKS; }
-
 hipError_t grad_norm(hipStream_t st, const float* g, int64_t n, double* part, float clip, float* norm_out,
                      float* scale_out, int* flags) {
   hipLaunchKernelGGL(norm_part_kernel, dim3(NORM_BLOCKS), dim3(256), 0, st, g, n, part);
@@ -894,13 +892,15 @@ hipError_t adamw(hipStream_t st, float* p, const float* g, float* m, float* v, v
 }
 
 hipError_t quant_rows(hipStream_t st, const void* x, fp8e4* q, float* scale, int rows, int K) {
-  if (K % 8 != 0 || K > 512 * 6) return hipErrorInvalidValue;
+  if (K % 8 != 0 || K > 512 * 8) return hipErrorInvalidValue;
   const dim3 grid((rows + 3) / 4);
   const bf16* xb = static_cast<const bf16*>(x);
   if (K <= 512 * 2)
     hipLaunchKernelGGL(quant_rows_kernel<2>, grid, dim3(256), 0, st, xb, q, scale, rows, K);
-  else
+  else if (K <= 512 * 6)
     hipLaunchKernelGGL(quant_rows_kernel<6>, grid, dim3(256), 0, st, xb, q, scale, rows, K);
+  else
+    hipLaunchKernelGGL(quant_rows_kernel<8>, grid, dim3(256), 0, st, xb, q, scale, rows, K);
   return hipGetLastError();
 }
 
@@ -917,12 +917,14 @@ hipError_t quant_jobs(hipStream_t st, const QuantJob* jobs, int count) {
     kmax = std::max(kmax, jobs[i].cols);
     if (jobs[i].cols % 8 != 0) return hipErrorInvalidValue;
   }
-  if (kmax > 512 * 6) return hipErrorInvalidValue;
+  if (kmax > 512 * 8) return hipErrorInvalidValue;
   const dim3 grid((rows + 3) / 4);
   if (kmax <= 512 * 2)
     hipLaunchKernelGGL(quant_jobs_kernel<2>, grid, dim3(256), 0, st, J);
-  else
+  else if (kmax <= 512 * 6)
     hipLaunchKernelGGL(quant_jobs_kernel<6>, grid, dim3(256), 0, st, J);
+  else
+    hipLaunchKernelGGL(quant_jobs_kernel<8>, grid, dim3(256), 0, st, J);
   return hipGetLastError();
 }
 
