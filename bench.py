@@ -7,10 +7,12 @@ cross-entropy, and their gradients) followed by global-norm clipping and
 AdamW, all in the HIP library.  Inputs are synthetic Zipf(s=1) token streams
 already resident in device memory; weights are a random GPT-2 init.
 
-Prints one JSON line: tokens/s (whole job), MFU against the bf16 dense MFMA
-peak, the roofline of the dominant kernel measured with HIP events on the
-library's stream during the timed steps, and the CPU oracle's throughput on a
-bounded sample of the same workload.
+Prints one JSON line: tokens/s (whole job, from the median step time; the
+mean is reported beside it), MFU against the bf16 dense MFMA peak, the
+roofline of the dominant kernel measured with HIP events around its launches
+in steps of their own after the timed region (the timed steps carry no
+per-kernel instrumentation), and the CPU oracle's throughput on a bounded
+sample of the same workload.
 
 Only one GPU is supported; --gpus > 1 exits with a message.
 """
@@ -58,42 +60,69 @@ def measured_traffic(kernel, workload):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(model, seed_stream, sample_tokens):
-    """The oracle (plain fp32 C++, not tuned) on one sample sequence of the
-    same workload: forward, backward, clip and AdamW over all parameters."""
+def host_cpu():
+    """Model name of the host CPU, the CPUs this process may run on, and the
+    threads the oracle's OpenMP loops use (OMP_NUM_THREADS when set, else one
+    per available CPU)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or avail
+    return model, avail, threads
+
+
+def cpu_baseline(model, seed_stream, B, T, B_full):
+    """The oracle (plain fp32 C++, not tuned) on a sample of the same workload:
+    a full training step (forward, backward, clip, AdamW over all parameters)
+    of B sequences of T tokens.  Its forward and backward cost is linear in the
+    tokens, so the sample's tokens/s is also the full batch's, except that the
+    update over all parameters is spread over fewer tokens (reported
+    separately, with the full-batch rate it implies)."""
     import numpy as np
 
     from oracle import oracle
     from transformer_lm_pretraining_gpt2_amd import synth
 
-    T = sample_tokens
     lay = oracle.param_layout(model)
     p = synth.init_params(lay, model.n_layer, model.vocab_size)
-    ids, tgt = synth.micro_batch(seed_stream, 1, T, 0)
+    ids, tgt = synth.micro_batch(seed_stream, B, T, 0)
     g = np.zeros_like(p)
     m = np.zeros_like(p)
     v = np.zeros_like(p)
     t0 = time.perf_counter()
-    oracle.fwd_bwd(model, 1, T, p, ids, tgt, 1.0, g, R=np.float32)
+    oracle.fwd_bwd(model, B, T, p, ids, tgt, 1.0, g, R=np.float32)
+    t1 = time.perf_counter()
     oracle.clip_grads(g, 1.0, R=np.float32)
     oracle.adamw(model, p, g, m, v, 1, 6e-4, R=np.float32)
-    dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", 0)) or os.cpu_count()
-    return {"value": T / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"one {T}-token sequence of the same model (B=1): fp32 forward+backward, clip and AdamW over all "
-                      f"{oracle.num_params(model)} parameters, {dt:.1f} s wall"}
+    t2 = time.perf_counter()
+    cpu, avail, threads = host_cpu()
+    full = B_full * T / ((t1 - t0) * B_full / B + (t2 - t1))
+    return {"value": B * T / (t2 - t0), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full step on {B} sequences of {T} tokens of the same model (B={B}): fp32 forward+backward "
+                      f"{t1 - t0:.1f} s, clip and AdamW over all {oracle.num_params(model)} parameters {t2 - t1:.1f} s",
+            "full_batch_estimate": {"value": full, "B": B_full,
+                                    "note": "forward+backward scaled linearly in tokens, one update"},
+            "host_cpu": cpu, "nproc": avail, "threads": threads}
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="gpt2_124m")
     ap.add_argument("--precision", default=None, help="fp32 or bf16 (default: the workload's)")
     ap.add_argument("--roofline-kernel", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=4,
+                    help="sequences in the oracle's timed sample step (about 5 s each at 124M on 16 cores)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="before warmup, one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--recompute", action="store_true",
@@ -131,12 +160,12 @@ def main():
     step = binding.TrainStep(model, B, T, prec, device=dev, recompute=args.recompute, fp8=args.fp8)
     lay = step.layout
     step.set_params(synth.init_params(lay, model.n_layer, model.vocab_size))
-    ISO = 2  # untimed steps after the timed region: the dominant kernel timed without overlap
-    n_tok = synth.stream_length(W + S + ISO, K, B, T)
+    RT, ISO = 3, 2  # steps after the timed region: the dominant kernel timed in the step, then alone
+    n_tok = synth.stream_length(W + S + RT + ISO, K, B, T)
     stream = synth.zipf_stream(n_tok, model.vocab_size) if rc.data == "zipf" else synth.uniform_stream(
         n_tok, model.vocab_size)
     # every micro-batch of the run, resident in HBM before timing starts
-    nmb = (W + S + ISO) * K
+    nmb = (W + S + RT + ISO) * K
     ids_all = np.empty((nmb, B * T), np.int32)
     tgt_all = np.empty((nmb, B * T), np.int32)
     for i in range(nmb):
@@ -170,36 +199,46 @@ def main():
         raise SystemExit(f"warmup step failed: {binding.ERRORS.get(st, st)}")
     first_loss = loss.item()
 
-    kname = args.roofline_kernel or DOMINANT.get(args.config, "gemm_tn_f32")
-    step.timing_enable(kname, True)
-    step.timing_read()
+    # The timed steps carry no per-kernel instrumentation: only one event on
+    # the caller's stream at each step boundary (for the median).
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(S + 1)]
     t0 = time.perf_counter()
-    ev0.record()
-    for s in range(W, W + S):
+    evs[0].record()
+    for j, s in enumerate(range(W, W + S)):
         one_step(s)
-    ev1.record()
+        evs[j + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    k_ms, k_launches, k_flops = step.timing_read()
     st = step.sync_status()
     if st != 0:
         raise SystemExit(f"timed step failed: {binding.ERRORS.get(st, st)}")
-    # the same kernel in isolation: the weight-gradient products overlap the
-    # rest of the backward in the timed steps, which stretches their launches
-    step.set_overlap(False)
+    step_ms = sorted(evs[j].elapsed_time(evs[j + 1]) for j in range(S))
+    median_ms = step_ms[S // 2] if S % 2 else 0.5 * (step_ms[S // 2 - 1] + step_ms[S // 2])
+    # The dominant kernel, timed afterwards in steps of their own: with HIP
+    # events around each of its launches on the stream it runs on, in the same
+    # overlapped schedule, then with overlap off (the kernel alone).
+    kname = args.roofline_kernel or DOMINANT.get(args.config, "gemm_tn_f32")
+    step.timing_enable(kname, True)
     step.timing_read()
-    for s in range(W + S, W + S + ISO):
+    for s in range(W + S, W + S + RT):
+        one_step(s)
+    k_ms, k_launches, k_flops = step.timing_read()
+    step.set_overlap(False)
+    for s in range(W + S + RT, W + S + RT + ISO):
         one_step(s)
     torch.cuda.synchronize()
     i_ms, i_launches, i_flops = step.timing_read()
     step.set_overlap(True)
     step.timing_enable(kname, False)
+    st = step.sync_status()
+    if st != 0:
+        raise SystemExit(f"roofline step failed: {binding.ERRORS.get(st, st)}")
 
     wall_ms = (t1 - t0) * 1000 / S
-    ev_ms = ev0.elapsed_time(ev1) / S
-    ms = max(wall_ms, ev_ms)
+    ev_ms = evs[0].elapsed_time(evs[S]) / S
+    mean_ms = max(wall_ms, ev_ms)
+    ms = median_ms
     tokens = K * B * T
     tps = tokens / (ms / 1000)
     fpt = flops_per_token(model, T, causal=True)
@@ -212,14 +251,15 @@ def main():
         traffic = measured_traffic(kname, args.config)
         roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": round(peak / 1e12, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
-                "avg_launch_us": round(1000 * k_ms / k_launches, 2), "launches_per_step": k_launches / S,
+                "avg_launch_us": round(1000 * k_ms / k_launches, 2), "launches_per_step": k_launches / RT,
                 "flops_per_launch": k_flops / k_launches,
-                "note": "timed region: these launches run on a second stream, overlapping the rest of the backward"}
+                "note": f"{RT} steps after the timed region, same schedule, with HIP events around each launch of "
+                        "this kernel on the stream it runs on"}
         if i_launches:
             ia = i_flops / (i_ms / 1000)
             roof["isolated"] = {"achieved": round(ia / 1e12, 2), "frac": round(ia / peak, 4),
                                 "avg_launch_us": round(1000 * i_ms / i_launches, 2), "steps": ISO,
-                                "note": "same kernel, overlap off, untimed steps after the timed region"}
+                                "note": "same kernel with overlap off (nothing runs beside it)"}
 
     out = {
         "metric": (METRIC if args.config == "gpt2_124m" and not args.fp8 else
@@ -230,6 +270,10 @@ def main():
         "steps": S,
         "warmup": W,
         "ms_per_step": round(ms, 3),
+        "ms_per_step_median": round(median_ms, 3),
+        "ms_per_step_mean": round(mean_ms, 3),
+        "ms_per_step_min": round(step_ms[0], 3),
+        "ms_per_step_max": round(step_ms[-1], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -253,7 +297,7 @@ def main():
                     "note": "pages' single-A100 figure (PyTorch, bf16, compile, flash attention); context only"},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(model, stream, min(args.cpu_sample_tokens, T))
+        out["cpu_baseline"] = cpu_baseline(model, stream, min(args.cpu_sample_seqs, B), T, B * K)
     print(json.dumps(out), flush=True)
 
 

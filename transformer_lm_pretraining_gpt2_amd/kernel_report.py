@@ -11,7 +11,9 @@ Inputs (all from `python3 bench.py --steps S --warmup W --no-cpu-baseline
   * a `--pmc FETCH_SIZE` and a `--pmc WRITE_SIZE` run: HBM bytes per dispatch,
     scaled by what the counters read for the plain N MiB device copy (see
     traffic.py).
-Achieved GB/s = (fetch + write bytes per dispatch) / average traced duration.
+Achieved GB/s = (fetch + write bytes per dispatch) / average traced duration,
+and its fraction of the 8 TB/s HBM peak (the roofline of the memory-bound
+kernels: LayerNorm, cross-entropy, AdamW, reductions, embeddings).
 
     python -m transformer_lm_pretraining_gpt2_amd.kernel_report STATS_CSV MFMA_CSV FETCH_CSV WRITE_CSV \\
         --copy-mib 1024 --steps 7
@@ -21,7 +23,8 @@ import collections
 import csv
 import re
 
-from transformer_lm_pretraining_gpt2_amd.config import MI355X_BF16_PEAK_FLOPS, MI355X_FP32_MFMA_PEAK_FLOPS
+from transformer_lm_pretraining_gpt2_amd.config import (MI355X_BF16_PEAK_FLOPS, MI355X_FP32_MFMA_PEAK_FLOPS,
+                                                        MI355X_HBM_BYTES_PER_S)
 from transformer_lm_pretraining_gpt2_amd.traffic import COPY, read
 
 
@@ -73,8 +76,8 @@ def main(argv=None):
 
     tot = sum(float(r["TotalDurationNs"]) for r in stats)
     print(f"Kernel time per step: {tot / a.steps / 1e6:.3f} ms; counter scales: FETCH x{fs:.3f}, WRITE x{ws:.3f}\n")
-    print("| ms/step | share | calls/step | avg us | MFMA util | HBM GB/s | kernel |")
-    print("|---:|---:|---:|---:|---:|---:|---|")
+    print("| ms/step | share | calls/step | avg us | MFMA util | HBM GB/s | HBM frac | kernel |")
+    print("|---:|---:|---:|---:|---:|---:|---:|---|")
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:a.top]:
         name, t, avg = r["Name"], float(r["TotalDurationNs"]), float(r["AverageNs"])
         u = mf.get(name)
@@ -87,7 +90,8 @@ def main(argv=None):
             gbs = bytes_ / avg  # bytes per ns = GB/s
         print(f"| {t / a.steps / 1e6:.3f} | {100 * t / tot:.1f}% | {int(r['Calls']) / a.steps:g} | {avg / 1e3:.1f} | "
               f"{'' if util is None or util < 0.005 else f'{100 * util:.1f}%'} | "
-              f"{'' if gbs is None else f'{gbs:,.0f}'} | `{short(name)}` |")
+              f"{'' if gbs is None else f'{gbs:,.0f}'} | "
+              f"{'' if gbs is None else f'{gbs * 1e9 / MI355X_HBM_BYTES_PER_S:.2f}'} | `{short(name)}` |")
 
 
 if __name__ == "__main__":
