@@ -226,6 +226,31 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps);
 int gpt2_adamw_step(gpt2_t* h, int step, float lr, float beta1, float beta2, float eps, float weight_decay,
                     float grad_clip, float* d_grad_norm);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight training loops, harnesses that forbid hipMalloc): the same
+ * clip + AdamW update as gpt2_adamw_step, on flat buffers the caller passes,
+ * with no handle, no workspace and no allocation.  Its scratch (the global
+ * norm's 1024 fp64 partial sums, the clip factor and the skip flag: 8448
+ * bytes) is a fixed file-scope device array of the library, one copy per GPU,
+ * held until the process ends.
+ *   params    fp32 [n], updated in place; params_lp bf16 [n] copy rewritten
+ *             from the updated params, or NULL
+ *   grads     fp32 [n], read only (the clip factor is applied on the fly)
+ *   adam_m, adam_v  fp32 [n] moments, updated in place
+ *   n         multiple of 4, 4 <= n <= 2^36; the first n_decay elements
+ *             (a multiple of 4, <= n) take weight decay
+ *   d_grad_norm  fp32 [1] device, required: receives the pre-clip norm; a
+ *             non-finite value there means the update was skipped
+ *   stream    hipStream_t (NULL = the null stream); nothing synchronises
+ * Pointers must be 16-byte aligned (params_lp 8-byte).  GPT2_ERR_ARG for bad
+ * arguments or sizes beyond the limit, before any device work; GPT2_ERR_HIP
+ * if a launch fails.  Every call on one GPU uses that GPU's scratch array, so
+ * calls that overlap on one GPU (concurrent streams or threads) race; calls
+ * ordered on one stream do not. */
+int gpt2_adamw_step_noalloc(float* params, void* params_lp, const float* grads, float* adam_m, float* adam_v,
+                            int64_t n, int64_t n_decay, int step, float lr, float beta1, float beta2, float eps,
+                            float weight_decay, float grad_clip, float* d_grad_norm, void* stream);
+
 /* Synchronises the stream and returns (then clears) the deferred device error
  * flags: GPT2_OK, GPT2_ERR_TOKEN_RANGE, GPT2_ERR_NONFINITE or GPT2_ERR_HIP. */
 int gpt2_sync_status(gpt2_t* h);

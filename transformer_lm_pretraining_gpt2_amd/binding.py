@@ -54,6 +54,7 @@ SIGNATURES = [
     ("gpt2_residual", _I, [_P, _I, ctypes.POINTER(_P)]),
     ("gpt2_backward", _I, [_P, _I, _I]),
     ("gpt2_adamw_step", _I, [_P, _I, _F, _F, _F, _F, _F, _F, _P]),
+    ("gpt2_adamw_step_noalloc", _I, [_P, _P, _P, _P, _P, _I64, _I64, _I, _F, _F, _F, _F, _F, _F, _P, _P]),
     ("gpt2_sync_status", _I, [_P]),
     ("gpt2_last_error", ctypes.c_char_p, [_P]),
     ("gpt2_strerror", ctypes.c_char_p, [_I]),
@@ -120,6 +121,21 @@ def workspace_bytes(m, B, T, precision):
 
 def check_shapes(m, B, T):
     return int(lib().gpt2_check_shapes(ctypes.byref(cconfig(m)), B, T))
+
+
+def adamw_step_noalloc(params, params_lp, grads, m, v, n_decay, step, lr, beta1=0.9, beta2=0.95, eps=1e-8,
+                       weight_decay=0.1, grad_clip=1.0, grad_norm=None, stream=None):
+    """gpt2_adamw_step_noalloc on torch device tensors (fp32 [n] params, grads,
+    m, v; bf16 [n] params_lp or None; fp32 [1] grad_norm), enqueued on `stream`
+    (default: torch's current stream).  Raises Gpt2Error on a refused call."""
+    import torch
+
+    st = stream if stream is not None else torch.cuda.current_stream()
+    p = lambda t: t.data_ptr() if t is not None else None
+    rc = lib().gpt2_adamw_step_noalloc(p(params), p(params_lp), p(grads), p(m), p(v), params.numel(), n_decay, step, lr,
+                                       beta1, beta2, eps, weight_decay, grad_clip, p(grad_norm), st.cuda_stream)
+    if rc != 0:
+        raise Gpt2Error(rc, "adamw_step_noalloc")
 
 
 def kernel_names():

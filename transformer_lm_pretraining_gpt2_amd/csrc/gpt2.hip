@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1024,6 +1025,79 @@ int gpt2_adamw_step(gpt2_t* h, int step, float lr, float beta1, float beta2, flo
   t.done();
   if (!rc && h->fp8) rc = quantize_weights(h);
   return rc;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Clip + AdamW without allocation.  The scratch of gpt2_adamw_step_noalloc
+// (the global norm's fp64 partial sums, the clip factor and the skip flag) is
+// this file-scope device array instead of a workspace: each GPU the library
+// runs on holds its own copy until the process ends.  Every word a call reads
+// is written earlier in the same call (all partials by the first norm kernel,
+// the clip factor and the skip flag by the second), so nothing needs clearing
+// between calls; calls that overlap on one GPU share the array and race.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int64_t kNoAllocPartOff = 0;                                  // double[kGradNormParts]
+constexpr int64_t kNoAllocScaleOff = 8 * (int64_t)kGradNormParts;      // float: clip factor
+constexpr int64_t kNoAllocFlagsOff = kNoAllocScaleOff + 16;             // int[4]: [1] non-finite, [2] skip
+constexpr int64_t kNoAllocScratchBytes = (kNoAllocFlagsOff + 16 + 255) / 256 * 256;
+constexpr int64_t kNoAllocMaxParams = (int64_t)1 << 36;                 // 64 Gi parameters
+constexpr int kNoAllocMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices] = {};
+
+// Device address of the current device's copy of the scratch array, looked up
+// once per device (the host-side name of the array is not a device address).
+hipError_t noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+int gpt2_adamw_step_noalloc(float* params, void* params_lp, const float* grads, float* adam_m, float* adam_v,
+                            int64_t n, int64_t n_decay, int step, float lr, float beta1, float beta2, float eps,
+                            float weight_decay, float grad_clip, float* d_grad_norm, void* stream) {
+  if (!params || !grads || !adam_m || !adam_v || !d_grad_norm) return GPT2_ERR_ARG;
+  auto aligned16 = [](const void* p) { return p == nullptr || reinterpret_cast<uintptr_t>(p) % 16 == 0; };
+  if (!aligned16(params) || !aligned16(grads) || !aligned16(adam_m) || !aligned16(adam_v) ||
+      reinterpret_cast<uintptr_t>(params_lp) % 8 != 0)
+    return GPT2_ERR_ARG;
+  if (n <= 0 || n % 4 != 0 || n > kNoAllocMaxParams || n_decay < 0 || n_decay > n || n_decay % 4 != 0 || step < 1)
+    return GPT2_ERR_ARG;
+  void* ptr = nullptr;
+  if (noalloc_scratch(&ptr) != hipSuccess) return GPT2_ERR_HIP;
+  char* base = static_cast<char*>(ptr);
+  double* part = reinterpret_cast<double*>(base + kNoAllocPartOff);
+  float* scale = reinterpret_cast<float*>(base + kNoAllocScaleOff);
+  int* flags = reinterpret_cast<int*>(base + kNoAllocFlagsOff);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (grad_norm(st, grads, n, part, grad_clip, d_grad_norm, scale, flags) != hipSuccess) return GPT2_ERR_HIP;
+  const double bc1 = 1.0 - std::pow((double)beta1, (double)step);
+  const double bc2 = 1.0 - std::pow((double)beta2, (double)step);
+  if (adamw(st, params, grads, adam_m, adam_v, params_lp, n, n_decay, lr, beta1, beta2, eps, weight_decay, (float)bc1,
+            (float)bc2, scale, flags) != hipSuccess)
+    return GPT2_ERR_HIP;
+  return GPT2_OK;
 }
 
 int gpt2_sync_status(gpt2_t* h) {
