@@ -292,6 +292,193 @@ __device__ __forceinline__ void dtl_schedule() {
 // its 256 registers.
 constexpr bool gemm_has_colsum(int at, int epi, int waves) { return at == 1 && epi == EPI_F32 && (waves == 4 || waves == 8); }
 
+// Epilogue of one output tile: acc holds this wave's (BM/WI) x (BN/WJ) block of
+// accumulators; smem is the block's LDS (free of operand tiles: the first
+// barrier below waits for every wave's last fragment reads).  UNROLL unrolls
+// the loops over passes and chunks (straight-line code lets the compiler count
+// the memory operations still in flight exactly, so a persistent block can
+// leave the stores outstanding while it moves on to the next tile).
+template <typename T, int BM, int BN, int WI, int WJ, int EPI, bool FP8, bool UNROLL>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const f32x16 (&acc)[BM / WI / 32][BN / WJ / 32],
+                                              char* smem, int i0, int j0, int split, int tid, int lane, int wi,
+                                              int wj) {
+  constexpr int NT = WI * WJ * 64;
+  constexpr int WTJ = BN / WJ;
+  constexpr int TI = BM / WI / 32, TJ = WTJ / 32;
+  constexpr int RP = BM / WI;  // output rows staged per pass (one row of waves)
+  constexpr int SLD = BN + 4;  // staging row length (floats)
+  typedef typename Frag<T>::type F;
+  const int lr = lane & 31, lg = lane >> 5;
+  // Epilogue, staged through LDS one row of waves at a time so every global
+  // access is a coalesced 16-byte run along an output row.  Accumulator r of
+  // lane l holds out[i][j] with i = tile row base + l%32 and
+  // j = tile col base + 8*(r/4) + 4*(l/32) + r%4.
+  float* stage = reinterpret_cast<float*>(smem);
+  constexpr int CPRW = BN / 8;  // 8-column chunks per staged row
+  // Each thread takes NCH 8-column chunks of the staged rows per pass.  Their
+  // columns are the same in every pass, so the bias is loaded once, before
+  // the passes; the inputs that depend on the row (residual, gelu', the
+  // accumulated partial) are loaded a batch at a time, every load of a batch
+  // issued before its first store, so a batch pays one memory latency rather
+  // than one per chunk (the stores might alias the inputs, so the compiler
+  // would not hoist the loads above them by itself).
+  constexpr int NCH = (RP * CPRW + NT - 1) / NT;
+  constexpr bool HAS_BIAS = EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID;
+  constexpr int NBV0 = NT % CPRW == 0 ? 1 : NCH;  // distinct bias chunks per thread
+  constexpr bool HOIST = HAS_BIAS && NBV0 <= 4;    // (else the bias is loaded with each chunk)
+  constexpr int NBV = HOIST ? NBV0 : 1;
+  // (batches measured: one chunk at a time is as fast or faster for gelu',
+  // the plain store and the fp32 partials, whose 8-wave kernels spill)
+  // (and a thread with several bias chunks takes all its chunks at once, so
+  // the bias array is indexed with constants)
+  constexpr int BATCH = NBV > 1 ? NCH : EPI == EPI_RESID ? (NCH < 3 ? NCH : 3) : EPI == EPI_GELU_BWD ? NCH : 1;
+  static_assert(NBV == 1 || BATCH == NCH, "bias chunk index must be a constant");
+  const bool use_bias = HAS_BIAS && (EPI != EPI_STORE || g.bias != nullptr);
+  // FP8 operands: the column scales of a thread's chunks (fixed columns, as the bias)
+  f32x8 sbv[FP8 ? NBV : 1];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int k = 0; k < NBV; k++) {
+      const int j = j0 + ((tid + k * NT) % CPRW) * 8;
+      sbv[k] = j < g.N ? ld8(g.scale_b + j) : f32x8{};
+    }
+  }
+  f32x8 bv[NBV];
+#pragma unroll
+  for (int k = 0; k < NBV; k++) {
+    const int j = j0 + ((tid + k * NT) % CPRW) * 8;
+    bv[k] = f32x8{};
+    if (HOIST && use_bias && j < g.N) bv[k] = ld8(g.bias + j);
+  }
+  constexpr int PASS_UNROLL = UNROLL ? WI : 1;
+#pragma unroll PASS_UNROLL
+  for (int pass = 0; pass < WI; pass++) {
+    // the row-dependent inputs (residual, gelu', accumulated partial) of a
+    // batch of chunks: the first batch's loads are issued before the staging
+    // barrier, so their latency overlaps the accumulators' trip through LDS
+    auto load_batch = [&](const int b0, f32x8 (&x)[BATCH], F (&u)[BATCH]) {
+#pragma unroll
+      for (int k = 0; k < BATCH; k++) {
+        const int c = tid + (b0 + k) * NT;
+        const int il = c / CPRW, jl = (c % CPRW) * 8;
+        const int i = i0 + pass * RP + il, j = j0 + jl;
+        if (b0 + k < NCH && c < RP * CPRW && i < g.M && j < g.N) {
+          if constexpr (EPI == EPI_RESID) x[k] = ld8(g.resid + (int64_t)i * g.ldr + j);
+          if constexpr (EPI == EPI_GELU_BWD) u[k] = ld8(static_cast<const T*>(g.aux) + (int64_t)i * g.ldaux + j);
+          if constexpr (EPI == EPI_F32) {
+            if (g.accumulate)
+              x[k] = ld8(static_cast<const float*>(g.C) + (int64_t)split * g.split_stride + (int64_t)i * g.ldc + j);
+          }
+        }
+      }
+    };
+    f32x8 x0[BATCH];
+    F u0[BATCH];
+    load_batch(0, x0, u0);
+    __syncthreads();  // operand tiles (or the previous pass) are no longer read
+    if (wi == pass) {
+#pragma unroll
+      for (int ti = 0; ti < TI; ti++)
+#pragma unroll
+        for (int tj = 0; tj < TJ; tj++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int il = ti * 32 + lr, jl = wj * WTJ + tj * 32 + 8 * q + 4 * lg;
+            *reinterpret_cast<f32x4*>(stage + il * SLD + jl) =
+                f32x4{acc[ti][tj][4 * q], acc[ti][tj][4 * q + 1], acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]};
+          }
+    }
+    __syncthreads();
+    auto chunk_batch = [&](const int b0) {
+      f32x8 x[BATCH];
+      F u[BATCH];
+      if (b0 == 0) {
+#pragma unroll
+        for (int k = 0; k < BATCH; k++) {
+          x[k] = x0[k];
+          u[k] = u0[k];
+        }
+      } else {
+        load_batch(b0, x, u);
+      }
+#pragma unroll
+      for (int k = 0; k < BATCH; k++) {
+        const int c = tid + (b0 + k) * NT;
+        const int il = c / CPRW, jl = (c % CPRW) * 8;
+        const int i = i0 + pass * RP + il, j = j0 + jl;
+        if (!(b0 + k < NCH && c < RP * CPRW && i < g.M && j < g.N)) continue;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl + 4);
+        f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const f32x8 bias = HOIST ? bv[NBV == 1 ? 0 : (b0 + k) % NBV] : (use_bias ? ld8(g.bias + j) : f32x8{});
+        if constexpr (FP8) {
+          static_assert(!FP8 || HOIST, "FP8 tiles keep their column scales in registers");
+          v *= sbv[NBV == 1 ? 0 : (b0 + k) % NBV] * g.scale_a[i];
+        }
+        if constexpr (EPI == EPI_STORE || EPI == EPI_F32) v *= g.alpha;
+        if constexpr (EPI == EPI_STORE) {
+          if (use_bias) v += bias;
+          F o;
+#pragma unroll
+          for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e]);
+          st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
+        } else if constexpr (EPI == EPI_GELU) {
+          // the backward needs only gelu' at the pre-activation: store that
+          // (from the fp32 value) next to the activation
+          v += bias;
+          F gu, o;
+          if (g.preact) {
+            // keep the rounded pre-activation; the activation comes from that
+            // same rounded value, so recomputing it later reproduces it exactly
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+              gu[e] = from_f<T>(v[e]);
+              o[e] = from_f<T>(gelu_tanh(to_f<T>(gu[e])));
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+              const float sg = gelu_sigmoid(v[e]);
+              gu[e] = from_f<T>(gelu_tanh_grad_s(v[e], sg));
+              o[e] = from_f<T>(v[e] * sg);
+            }
+          }
+          if (g.aux) st8(static_cast<T*>(g.aux) + (int64_t)i * g.ldaux + j, gu);  // (none when evaluating)
+          st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
+        } else if constexpr (EPI == EPI_RESID) {
+          v += bias;
+          v += x[k];
+          st8(static_cast<float*>(g.C) + (int64_t)i * g.ldc + j, v);
+        } else if constexpr (EPI == EPI_GELU_BWD) {
+          F o;
+          if (g.preact) {
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+              const float x = to_f<T>(u[k][e]);
+              o[e] = from_f<T>(v[e] * gelu_tanh_grad_s(x, gelu_sigmoid(x)));
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e] * to_f<T>(u[k][e]));
+          }
+          st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
+        } else {  // EPI_F32
+          float* Cp = static_cast<float*>(g.C) + (int64_t)split * g.split_stride + (int64_t)i * g.ldc + j;
+          if (g.accumulate) v += x[k];
+          st8(Cp, v);
+        }
+      }
+    };
+    if constexpr (BATCH == 1 && !UNROLL) {
+#pragma unroll 1
+      for (int b0 = 0; b0 < NCH; b0++) chunk_batch(b0);
+    } else {
+#pragma unroll
+      for (int b0 = 0; b0 < NCH; b0 += BATCH) chunk_batch(b0);
+    }
+  }
+}
+
 // NBUF = 0: operands staged through registers (two register stages, two LDS
 // buffers).  NBUF >= 2 (bf16): direct-to-LDS loads into a ring of NBUF LDS
 // buffers, the tile NBUF steps ahead loading while the current one is used.
@@ -543,9 +730,6 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
 #undef GEMM_DTL_TILE
 #undef GEMM_DFRAGS
 #undef GEMM_MAINLOOP
-#undef GEMM_COMPUTE
-#undef GEMM_COMPUTE_ST
-#undef GEMM_FRAGS
   if (do_cs && wj == 0) {
 #pragma unroll
     for (int ti = 0; ti < TI; ti++) {
@@ -554,174 +738,162 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
       if (lane < 32 && i < g.M) g.colsum[(int64_t)split * g.colsum_stride + i] = t;
     }
   }
-  const int lr = lane & 31, lg = lane >> 5;
-  // Epilogue, staged through LDS one row of waves at a time so every global
-  // access is a coalesced 16-byte run along an output row.  Accumulator r of
-  // lane l holds out[i][j] with i = tile row base + l%32 and
-  // j = tile col base + 8*(r/4) + 4*(l/32) + r%4.
-  float* stage = reinterpret_cast<float*>(smem);
-  constexpr int CPRW = BN / 8;  // 8-column chunks per staged row
-  // Each thread takes NCH 8-column chunks of the staged rows per pass.  Their
-  // columns are the same in every pass, so the bias is loaded once, before
-  // the passes; the inputs that depend on the row (residual, gelu', the
-  // accumulated partial) are loaded a batch at a time, every load of a batch
-  // issued before its first store, so a batch pays one memory latency rather
-  // than one per chunk (the stores might alias the inputs, so the compiler
-  // would not hoist the loads above them by itself).
-  constexpr int NCH = (RP * CPRW + NT - 1) / NT;
-  constexpr bool HAS_BIAS = EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_RESID;
-  constexpr int NBV0 = NT % CPRW == 0 ? 1 : NCH;  // distinct bias chunks per thread
-  constexpr bool HOIST = HAS_BIAS && NBV0 <= 4;    // (else the bias is loaded with each chunk)
-  constexpr int NBV = HOIST ? NBV0 : 1;
-  // (batches measured: one chunk at a time is as fast or faster for gelu',
-  // the plain store and the fp32 partials, whose 8-wave kernels spill)
-  // (and a thread with several bias chunks takes all its chunks at once, so
-  // the bias array is indexed with constants)
-  constexpr int BATCH = NBV > 1 ? NCH : EPI == EPI_RESID ? (NCH < 3 ? NCH : 3) : EPI == EPI_GELU_BWD ? NCH : 1;
-  static_assert(NBV == 1 || BATCH == NCH, "bias chunk index must be a constant");
-  const bool use_bias = HAS_BIAS && (EPI != EPI_STORE || g.bias != nullptr);
-  // FP8 operands: the column scales of a thread's chunks (fixed columns, as the bias)
-  f32x8 sbv[FP8 ? NBV : 1];
-  if constexpr (FP8) {
+  gemm_epilogue<T, BM, BN, WI, WJ, EPI, FP8, false>(g, acc, smem, i0, j0, split, tid, lane, wi, wj);
+}
+
+// Persistent variant for forward and input-gradient products with several
+// rounds of output tiles (A reduction-contiguous, operands staged through
+// registers, an even number of reduction steps).  Each block walks a
+// sequence of output tiles.  While it computes the last two reduction steps
+// of a tile it loads the first two of its next tile, before the epilogue, so
+// the next tile starts without waiting for memory, the epilogue's stores
+// drain while it runs, and no block is launched per tile.  The tiles of one
+// XCD form one contiguous range in the grouped order of gemm_kernel, walked
+// by that XCD's blocks in turn.
+template <typename T, int BM, int BN, int BK, int WI, int WJ, int BT, int EPI>
+__global__ void __launch_bounds__(WI * WJ * 64) gemm_persist_kernel(GemmArgs g) {
+  constexpr int AT = 0;
+  constexpr int NT = WI * WJ * 64;
+  constexpr int WTI = BM / WI, WTJ = BN / WJ;
+  constexpr int TI = WTI / 32, TJ = WTJ / 32;
+  constexpr int NSUB = BK / 16;
+  typedef Operand<T, BM, BK, NT, AT> OA;
+  typedef Operand<T, BN, BK, NT, BT> OB;
+  typedef typename Frag<T>::type FI;
+  constexpr int OPER_BYTES = 2 * (OA::ELEMS + OB::ELEMS) * (int)sizeof(T);
+  constexpr int STAGE_BYTES = (BM / WI) * (BN + 4) * 4;
+  __shared__ __attribute__((aligned(16))) char smem[OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES];
+  T (*sA)[OA::ELEMS] = reinterpret_cast<T (*)[OA::ELEMS]>(smem);
+  T (*sB)[OB::ELEMS] = reinterpret_cast<T (*)[OB::ELEMS]>(smem + 2 * OA::ELEMS * sizeof(T));
+  constexpr bool PIPE = true, CSV = false, ILV = NSUB >= 4;
+  float cs[TI];  // (no bias-gradient sums here; named for the shared compute macros)
+  (void)cs;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+  const int wi = wave / WJ, wj = wave % WJ;
+  const int nbi = (g.M + BM - 1) / BM, nbj = (g.N + BN - 1) / BN, ntiles = nbi * nbj;
+  const int nk = g.K / BK;  // even, >= 2 (checked by the launcher)
+  // this XCD's range of logical tiles and this block's slot in it
+  const int x = blockIdx.x % 8, slot = blockIdx.x / 8, per = gridDim.x / 8;
+  const int q8 = ntiles / 8, r8 = ntiles % 8;
+  const int start = x < r8 ? x * (q8 + 1) : r8 * (q8 + 1) + (x - r8) * q8;
+  const int cnt = q8 + (x < r8 ? 1 : 0);
+  int li = slot;
+  if (li >= cnt) return;
+  constexpr int GM = 4;
+  auto coords = [&](int l, int& i0, int& j0) {
+    const int tile = start + l;
+    const int group = tile / (GM * nbj);
+    const int first_i = group * GM;
+    const int gsize = min(nbi - first_i, GM);
+    const int tig = tile - group * GM * nbj;
+    i0 = (first_i + tig % gsize) * BM;
+    j0 = (tig / gsize) * BN;
+  };
+  const T* A = static_cast<const T*>(g.A);
+  const T* Bm = static_cast<const T*>(g.B);
+  int i0, j0;
+  coords(li, i0, j0);
+  OA a0, a1;
+  OB b0, b1;
+  a0.init(A, g.lda, i0, g.M, tid);
+  b0.init(Bm, g.ldb, j0, g.N, tid);
+  a1.init(A, g.lda, i0, g.M, tid);
+  b1.init(Bm, g.ldb, j0, g.N, tid);
+  a0.load(0);
+  b0.load(0);
+  a1.load(BK);
+  b1.load(BK);
+  a0.store(sA[0], tid);
+  b0.store(sB[0], tid);
+  __syncthreads();
+  while (true) {
+    f32x16 acc[TI][TJ];
 #pragma unroll
-    for (int k = 0; k < NBV; k++) {
-      const int j = j0 + ((tid + k * NT) % CPRW) * 8;
-      sbv[k] = j < g.N ? ld8(g.scale_b + j) : f32x8{};
-    }
-  }
-  f32x8 bv[NBV];
+    for (int ti = 0; ti < TI; ti++)
 #pragma unroll
-  for (int k = 0; k < NBV; k++) {
-    const int j = j0 + ((tid + k * NT) % CPRW) * 8;
-    bv[k] = f32x8{};
-    if (HOIST && use_bias && j < g.N) bv[k] = ld8(g.bias + j);
-  }
-#pragma unroll 1
-  for (int pass = 0; pass < WI; pass++) {
-    // the row-dependent inputs (residual, gelu', accumulated partial) of a
-    // batch of chunks: the first batch's loads are issued before the staging
-    // barrier, so their latency overlaps the accumulators' trip through LDS
-    auto load_batch = [&](const int b0, f32x8 (&x)[BATCH], F (&u)[BATCH]) {
-#pragma unroll
-      for (int k = 0; k < BATCH; k++) {
-        const int c = tid + (b0 + k) * NT;
-        const int il = c / CPRW, jl = (c % CPRW) * 8;
-        const int i = i0 + pass * RP + il, j = j0 + jl;
-        if (b0 + k < NCH && c < RP * CPRW && i < g.M && j < g.N) {
-          if constexpr (EPI == EPI_RESID) x[k] = ld8(g.resid + (int64_t)i * g.ldr + j);
-          if constexpr (EPI == EPI_GELU_BWD) u[k] = ld8(static_cast<const T*>(g.aux) + (int64_t)i * g.ldaux + j);
-          if constexpr (EPI == EPI_F32) {
-            if (g.accumulate)
-              x[k] = ld8(static_cast<const float*>(g.C) + (int64_t)split * g.split_stride + (int64_t)i * g.ldc + j);
-          }
-        }
+      for (int tj = 0; tj < TJ; tj++) acc[ti][tj] = f32x16{};
+    const int lnext = li + per;
+    const bool has_next = lnext < cnt;
+    int i0n = i0, j0n = j0;  // (without a next tile: harmless re-reads of this one)
+    if (has_next) coords(lnext, i0n, j0n);
+    for (int kt = 0; kt + 4 <= nk; kt += 2) {
+      /* buffer 0 holds step kt, registers 1 hold step kt+1 */
+      a0.load((kt + 2) * BK);
+      b0.load((kt + 2) * BK);
+      if constexpr (ILV) {
+        GEMM_COMPUTE_ST(sA[0], sB[0], CSV, PIPE,
+                        (a1.template store_part<NSUB>(sA[1], tid, ks), b1.template store_part<NSUB>(sB[1], tid, ks)))
+      } else {
+        GEMM_COMPUTE(sA[0], sB[0], CSV, PIPE)
+        a1.store(sA[1], tid);
+        b1.store(sB[1], tid);
       }
-    };
-    f32x8 x0[BATCH];
-    F u0[BATCH];
-    load_batch(0, x0, u0);
-    __syncthreads();  // operand tiles (or the previous pass) are no longer read
-    if (wi == pass) {
-#pragma unroll
-      for (int ti = 0; ti < TI; ti++)
-#pragma unroll
-        for (int tj = 0; tj < TJ; tj++)
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const int il = ti * 32 + lr, jl = wj * WTJ + tj * 32 + 8 * q + 4 * lg;
-            *reinterpret_cast<f32x4*>(stage + il * SLD + jl) =
-                f32x4{acc[ti][tj][4 * q], acc[ti][tj][4 * q + 1], acc[ti][tj][4 * q + 2], acc[ti][tj][4 * q + 3]};
-          }
+      __syncthreads();
+      a1.load((kt + 3) * BK);
+      b1.load((kt + 3) * BK);
+      if constexpr (ILV) {
+        GEMM_COMPUTE_ST(sA[1], sB[1], CSV, PIPE,
+                        (a0.template store_part<NSUB>(sA[0], tid, ks), b0.template store_part<NSUB>(sB[0], tid, ks)))
+      } else {
+        GEMM_COMPUTE(sA[1], sB[1], CSV, PIPE)
+        a0.store(sA[0], tid);
+        b0.store(sB[0], tid);
+      }
+      __syncthreads();
+    }
+    // the last two steps (nk-2 in buffer 0, nk-1 in registers 1); the
+    // registers 0 and then 1 take the next tile's first two steps
+    a0.init(A, g.lda, i0n, g.M, tid);
+    b0.init(Bm, g.ldb, j0n, g.N, tid);
+    a0.load(0);
+    b0.load(0);
+    if constexpr (ILV) {
+      GEMM_COMPUTE_ST(sA[0], sB[0], CSV, PIPE,
+                      (a1.template store_part<NSUB>(sA[1], tid, ks), b1.template store_part<NSUB>(sB[1], tid, ks)))
+    } else {
+      GEMM_COMPUTE(sA[0], sB[0], CSV, PIPE)
+      a1.store(sA[1], tid);
+      b1.store(sB[1], tid);
     }
     __syncthreads();
-    auto chunk_batch = [&](const int b0) {
-      f32x8 x[BATCH];
-      F u[BATCH];
-      if (b0 == 0) {
-#pragma unroll
-        for (int k = 0; k < BATCH; k++) {
-          x[k] = x0[k];
-          u[k] = u0[k];
-        }
-      } else {
-        load_batch(b0, x, u);
-      }
-#pragma unroll
-      for (int k = 0; k < BATCH; k++) {
-        const int c = tid + (b0 + k) * NT;
-        const int il = c / CPRW, jl = (c % CPRW) * 8;
-        const int i = i0 + pass * RP + il, j = j0 + jl;
-        if (!(b0 + k < NCH && c < RP * CPRW && i < g.M && j < g.N)) continue;
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(stage + il * SLD + jl + 4);
-        f32x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const f32x8 bias = HOIST ? bv[NBV == 1 ? 0 : (b0 + k) % NBV] : (use_bias ? ld8(g.bias + j) : f32x8{});
-        if constexpr (FP8) {
-          static_assert(!FP8 || HOIST, "FP8 tiles keep their column scales in registers");
-          v *= sbv[NBV == 1 ? 0 : (b0 + k) % NBV] * g.scale_a[i];
-        }
-        if constexpr (EPI == EPI_STORE || EPI == EPI_F32) v *= g.alpha;
-        if constexpr (EPI == EPI_STORE) {
-          if (use_bias) v += bias;
-          F o;
-#pragma unroll
-          for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e]);
-          st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
-        } else if constexpr (EPI == EPI_GELU) {
-          // the backward needs only gelu' at the pre-activation: store that
-          // (from the fp32 value) next to the activation
-          v += bias;
-          F gu, o;
-          if (g.preact) {
-            // keep the rounded pre-activation; the activation comes from that
-            // same rounded value, so recomputing it later reproduces it exactly
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-              gu[e] = from_f<T>(v[e]);
-              o[e] = from_f<T>(gelu_tanh(to_f<T>(gu[e])));
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-              const float sg = gelu_sigmoid(v[e]);
-              gu[e] = from_f<T>(gelu_tanh_grad_s(v[e], sg));
-              o[e] = from_f<T>(v[e] * sg);
-            }
-          }
-          if (g.aux) st8(static_cast<T*>(g.aux) + (int64_t)i * g.ldaux + j, gu);  // (none when evaluating)
-          st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
-        } else if constexpr (EPI == EPI_RESID) {
-          v += bias;
-          v += x[k];
-          st8(static_cast<float*>(g.C) + (int64_t)i * g.ldc + j, v);
-        } else if constexpr (EPI == EPI_GELU_BWD) {
-          F o;
-          if (g.preact) {
-#pragma unroll
-            for (int e = 0; e < 8; e++) {
-              const float x = to_f<T>(u[k][e]);
-              o[e] = from_f<T>(v[e] * gelu_tanh_grad_s(x, gelu_sigmoid(x)));
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < 8; e++) o[e] = from_f<T>(v[e] * to_f<T>(u[k][e]));
-          }
-          st8(static_cast<T*>(g.C) + (int64_t)i * g.ldc + j, o);
-        } else {  // EPI_F32
-          float* Cp = static_cast<float*>(g.C) + (int64_t)split * g.split_stride + (int64_t)i * g.ldc + j;
-          if (g.accumulate) v += x[k];
-          st8(Cp, v);
-        }
-      }
-    };
-    if constexpr (BATCH == 1) {
-#pragma unroll 1
-      for (int b0 = 0; b0 < NCH; b0++) chunk_batch(b0);
-    } else {
-#pragma unroll
-      for (int b0 = 0; b0 < NCH; b0 += BATCH) chunk_batch(b0);
-    }
+    a1.init(A, g.lda, i0n, g.M, tid);
+    b1.init(Bm, g.ldb, j0n, g.N, tid);
+    a1.load(BK);
+    b1.load(BK);
+    GEMM_COMPUTE(sA[1], sB[1], CSV, PIPE)
+    gemm_epilogue<T, BM, BN, WI, WJ, EPI, false, true>(g, acc, smem, i0, j0, 0, tid, lane, wi, wj);
+    if (!has_next) break;
+    __syncthreads();  // every wave has read its last staged chunk
+    a0.store(sA[0], tid);
+    b0.store(sB[0], tid);
+    __syncthreads();
+    li = lnext;
+    i0 = i0n;
+    j0 = j0n;
   }
+}
+
+#undef GEMM_COMPUTE
+#undef GEMM_COMPUTE_ST
+#undef GEMM_FRAGS
+
+// Blocks of a persistent launch: one per CU with a one-block-per-CU tile
+// (256 CUs), rounded down to a multiple of the 8 XCDs; never more than the
+// tiles.
+constexpr int kPersistBlocks = 256;
+
+template <typename T, int BM, int BN, int WI, int WJ, int BT, int EPI, int BK>
+hipError_t launch_persist(hipStream_t st, const GemmArgs& g) {
+  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.K <= 0 || g.K % (2 * BK) != 0 || g.M % 8 != 0 || g.N % 8 != 0 || g.lda % 8 != 0 || g.ldb % 8 != 0 ||
+      g.splits != 1 || g.colsum != nullptr || EPI == EPI_F32)
+    return hipErrorInvalidValue;
+  const int ntiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  int blocks = std::min(kPersistBlocks, ntiles);
+  blocks = std::max(8, blocks / 8 * 8);
+  hipLaunchKernelGGL((gemm_persist_kernel<T, BM, BN, BK, WI, WJ, BT, EPI>), dim3(blocks), dim3(WI * WJ * 64), 0, st, g);
+  return hipGetLastError();
 }
 
 template <typename T, int BM, int BN, int WI, int WJ, int AT, int BT, int EPI, int BK, int NBUF = 0, typename TIn = T>
@@ -759,22 +931,39 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
 //    buffers, BK = 64): other forward products up to 4096 wide (both operands
 //    reduction-contiguous), where it saves the staging registers.  Its single
 //    tile of look-ahead is too short for the tied head's long sweep.
+//  * TILE_P256_W8 / TILE_P192_W8: the persistent versions of the two 8-wave
+//    tiles (gemm_persist_kernel) for products with more than one round of
+//    tiles (more tiles than CUs) and an even number of reduction steps: at
+//    124M the qkv and tied-head forward products and the MLP's input
+//    gradient (66 vs 70 us, 1347 vs 1487 us, 92 vs 104 us, interleaved runs
+//    on one box).  The 256x192 tile also serves the MLP input gradient, whose
+//    GELU' epilogue spills registers on the 256x256 one.
 enum TileKind {
-  TILE_128 = 0, TILE_128_K32, TILE_256x192_K32, TILE_256_W8, TILE_256_W8_K32, TILE_D256_W8, TILE_192_W8
+  TILE_128 = 0, TILE_128_K32, TILE_256x192_K32, TILE_256_W8, TILE_256_W8_K32, TILE_D256_W8, TILE_192_W8,
+  TILE_P256_W8, TILE_P192_W8
 };
 
 TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
   if (p != BF16 || M < 256) return TILE_128;
   const int64_t mn = (int64_t)M * N;
   if (a_t && b_t) return TILE_256_W8_K32;
-  if (N % 192 == 0 && N <= 2304 && mn >= 4000000) return TILE_192_W8;
-  if (K >= 2048 || mn >= 40000000) return (!a_t && !b_t && N <= 4096) ? TILE_D256_W8 : TILE_256_W8;
+  auto rounds = [&](int bn) { return (int64_t)((M + 255) / 256) * ((N + bn - 1) / bn) > kPersistBlocks; };
+  const bool even = K % 128 == 0;  // an even number of 64-deep reduction steps
+  // 192-wide outputs: the model-width products, the qkv projection, and the
+  // MLP's input gradient (whose GELU' epilogue spills on the 256-wide tile)
+  if (N % 192 == 0 && (N <= 2304 || b_t) && mn >= 4000000)
+    return !a_t && even && rounds(192) ? TILE_P192_W8 : TILE_192_W8;
+  if (K >= 2048 || mn >= 40000000) {
+    if (!a_t && !b_t && N <= 4096) return TILE_D256_W8;
+    return !a_t && !b_t && even && rounds(256) ? TILE_P256_W8 : TILE_256_W8;
+  }
   return TILE_128;
 }
 
 int tile_bk(Prec p, TileKind k) {
   if (p != BF16) return 32;
-  return (k == TILE_128 || k == TILE_256_W8 || k == TILE_D256_W8 || k == TILE_192_W8) ? 64 : 32;
+  return (k == TILE_128 || k == TILE_256_W8 || k == TILE_D256_W8 || k == TILE_192_W8 || k == TILE_P256_W8 ||
+          k == TILE_P192_W8) ? 64 : 32;
 }
 
 template <typename T, int AT, int BT, int EPI>
@@ -785,6 +974,10 @@ hipError_t launch_tiled(hipStream_t st, const GemmArgs& g, TileKind k) {
     }
     if constexpr (AT == 0) {
       if (k == TILE_192_W8) return launch<T, 256, 192, 4, 2, AT, BT, EPI, 64>(st, g);
+      if constexpr (EPI != EPI_F32) {
+        if (k == TILE_P192_W8) return launch_persist<T, 256, 192, 4, 2, BT, EPI, 64>(st, g);
+        if (k == TILE_P256_W8) return launch_persist<T, 256, 256, 2, 4, BT, EPI, 64>(st, g);
+      }
     }
     if (k == TILE_256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI, 64>(st, g);
     if constexpr (AT == 1) {
@@ -837,8 +1030,8 @@ hipError_t gemm_fp8(hipStream_t st, int epi, const GemmArgs& g) {
 int gemm_split_hint(Prec p, int a_t, int b_t, int M, int N, int K) {
   const TileKind k = choose_tile(p, a_t, b_t, M, N, K);
   const int bm = (k == TILE_128 || k == TILE_128_K32) ? 128 : 256;
-  const int bn = (k == TILE_256x192_K32 || k == TILE_192_W8) ? 192
-                 : (k == TILE_256_W8 || k == TILE_256_W8_K32 || k == TILE_D256_W8) ? 256 : 128;
+  const int bn = (k == TILE_256x192_K32 || k == TILE_192_W8 || k == TILE_P192_W8) ? 192
+                 : (k == TILE_256_W8 || k == TILE_256_W8_K32 || k == TILE_D256_W8 || k == TILE_P256_W8) ? 256 : 128;
   const int bk = tile_bk(p, k);
   const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
   if (a_t && b_t && k == TILE_256_W8_K32) {
