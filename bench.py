@@ -129,6 +129,8 @@ def main():
                     help="activation recompute for the MLP (smaller workspace, one extra pass per layer)")
     ap.add_argument("--fp8", action="store_true",
                     help="forward products on FP8 E4M3 copies (per-row scales); reported as its own dtype")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="run the whole step on one stream (no second stream for the weight gradients)")
     ap.add_argument("--mode", choices=["train", "eval"], default="train",
                     help="eval: forward-only validation loss over held-out batches instead of the training step")
     args = ap.parse_args()
@@ -158,6 +160,7 @@ def main():
     dev = torch.device("cuda:0")
 
     step = binding.TrainStep(model, B, T, prec, device=dev, recompute=args.recompute, fp8=args.fp8)
+    step.set_overlap(not args.no_overlap)
     lay = step.layout
     step.set_params(synth.init_params(lay, model.n_layer, model.vocab_size))
     RT, ISO = 3, 2  # steps after the timed region: the dominant kernel timed in the step, then alone
@@ -229,7 +232,7 @@ def main():
         one_step(s)
     torch.cuda.synchronize()
     i_ms, i_launches, i_flops = step.timing_read()
-    step.set_overlap(True)
+    step.set_overlap(not args.no_overlap)
     step.timing_enable(kname, False)
     st = step.sync_status()
     if st != 0:
@@ -289,6 +292,7 @@ def main():
                                f"->{model.padded_vocab_size}",
                    "global_batch": B * K, "seq_len": T, "grad_accum": K, "parallelism": "none (1 GPU)",
                    "activation_recompute": bool(args.recompute), "fp8_forward": bool(args.fp8),
+                   "two_streams": not args.no_overlap,
                    "workspace_bytes": int(step.workspace.numel())},
         "roofline": roof,
         "loss_first_timed": round(first_loss, 4),

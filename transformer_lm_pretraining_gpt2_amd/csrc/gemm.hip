@@ -486,7 +486,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const f32x16 (&
 // contiguous operands, register staging, acc(i, j) scaled by scale_a[i] *
 // scale_b[j] before the epilogue).
 template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI, int NBUF, typename TIn>
-__global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split) {
   constexpr int NT = WI * WJ * 64;
   constexpr int WTI = BM / WI, WTJ = BN / WJ;
   constexpr int TI = WTI / 32, TJ = WTJ / 32;
@@ -514,18 +514,6 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wi = wave / WJ, wj = wave % WJ;
   const int nbi = (g.M + BM - 1) / BM, nbj = (g.N + BN - 1) / BN;
-  // With a split reduction each XCD takes a contiguous range of (split, tile)
-  // pairs in split-major order, so the token rows one split reads are fetched
-  // by one or two XCDs' L2 instead of all eight.
-  int tile, split = 0;
-  if (gridDim.y > 1) {
-    const int nt = nbi * nbj;
-    const int logical = xcd_remap_any(blockIdx.x + blockIdx.y * nt, nt * gridDim.y);
-    split = logical / nt;
-    tile = logical % nt;
-  } else {
-    tile = xcd_remap(blockIdx.x, nbi * nbj);
-  }
   // Grouped tile order: GM consecutive row-tiles sweep the columns together.
   constexpr int GM = 4;
   const int group = tile / (GM * nbj);
@@ -739,6 +727,37 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
     }
   }
   gemm_epilogue<T, BM, BN, WI, WJ, EPI, FP8, false>(g, acc, smem, i0, j0, split, tid, lane, wi, wj);
+}
+
+template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI, int NBUF, typename TIn>
+__global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
+  const int nt = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  // With a split reduction each XCD takes a contiguous range of (split, tile)
+  // pairs in split-major order, so the token rows one split reads are fetched
+  // by one or two XCDs' L2 instead of all eight.
+  if (gridDim.y > 1) {
+    const int logical = xcd_remap_any(blockIdx.x + blockIdx.y * nt, nt * gridDim.y);
+    gemm_body<T, BM, BN, BK, WI, WJ, AT, BT, EPI, NBUF, TIn>(g, logical % nt, logical / nt);
+  } else {
+    gemm_body<T, BM, BN, BK, WI, WJ, AT, BT, EPI, NBUF, TIn>(g, xcd_remap(blockIdx.x, nt), 0);
+  }
+}
+
+// Several independent products of one shape class in one launch (the weight
+// gradients of a layer): problem p owns the logical blocks [block0[p],
+// block0[p+1]), split-major inside it as in gemm_kernel; the blocks are
+// renumbered so each XCD takes one contiguous range of logical blocks.
+template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI>
+__global__ void __launch_bounds__(WI * WJ * 64) gemm_group_kernel(GemmGroup gg) {
+  const int logical = xcd_remap_any(blockIdx.x, gg.block0[gg.count]);
+  int p = 0;
+#pragma unroll
+  for (int q = 1; q < kMaxGemmGroup; q++)
+    if (q < gg.count && logical >= gg.block0[q]) p = q;
+  const GemmArgs& g = gg.p[p];
+  const int nt = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  const int local = logical - gg.block0[p];
+  gemm_body<T, BM, BN, BK, WI, WJ, AT, BT, EPI, 0, T>(g, local % nt, local / nt);
 }
 
 // Persistent variant for forward and input-gradient products with several
@@ -1011,6 +1030,38 @@ hipError_t dispatch(hipStream_t st, int a_t, int b_t, int epi, const GemmArgs& g
 hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArgs& g) {
   const TileKind k = choose_tile(p, a_t, b_t, g.M, g.N, g.K);
   return p == BF16 ? dispatch<bf16>(st, a_t, b_t, epi, g, k) : dispatch<float>(st, a_t, b_t, epi, g, k);
+}
+
+int gemm_group_tiles(int M, int N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+
+int gemm_group_split_hint(int M, int N, int K, int group_tiles) {
+  // the weight-gradient tile (256x256, BK = 32): as many splits as keep the
+  // group's blocks within one round over the CUs, each at least two steps long
+  (void)M;
+  (void)N;
+  if (group_tiles <= 0 || group_tiles >= 256) return 1;
+  return std::max(1, std::min(256 / group_tiles, K / 32 / 2));
+}
+
+hipError_t gemm_group(hipStream_t st, const GemmArgs* probs, int count) {
+  constexpr int BM = 256, BN = 256, BK = 32, WI = 2, WJ = 4;
+  if (count < 1 || count > kMaxGemmGroup) return hipErrorInvalidValue;
+  GemmGroup gg;
+  gg.count = count;
+  int blocks = 0;
+  for (int i = 0; i < count; i++) {
+    const GemmArgs& g = probs[i];
+    if (g.M <= 0 || g.N <= 0 || g.K <= 0 || g.splits < 1 || g.K % BK != 0 || g.K / BK < g.splits || g.M % 8 != 0 ||
+        g.N % 8 != 0 || g.lda % 8 != 0 || g.ldb % 8 != 0)
+      return hipErrorInvalidValue;
+    gg.p[i] = g;
+    gg.block0[i] = blocks;
+    blocks += ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN) * g.splits;
+  }
+  for (int i = count; i <= kMaxGemmGroup; i++) gg.block0[i] = blocks;
+  hipLaunchKernelGGL((gemm_group_kernel<bf16, BM, BN, BK, WI, WJ, 1, 1, EPI_F32>), dim3(blocks), dim3(WI * WJ * 64), 0,
+                     st, gg);
+  return hipGetLastError();
 }
 
 hipError_t gemm_fp8(hipStream_t st, int epi, const GemmArgs& g) {

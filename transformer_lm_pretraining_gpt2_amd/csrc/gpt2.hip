@@ -133,7 +133,16 @@ struct Plan {
   // sums can be reduced by one launch: weight kinds (qkv, proj, fc, fcproj)
   // for the split-K products and their bias column sums; LayerNorm slots
   // (final, ln_2, ln_1) for the gain/bias partials
-  int64_t wpart[4], cspart[4], lnpart[4];  // LayerNorm partials: final, LN2 (even, odd layers), LN1
+  int64_t wpart[4], cspart[4];
+  // LayerNorm partials: final, LN2 (even, odd layers), LN1 (even, odd layers)
+  int64_t lnpart[5];
+  // bf16: the second matmul copy of dres (odd layers' block-output gradient
+  // when the weight gradients of a layer run as one grouped launch)
+  int64_t dres_lp2 = -1;
+  // grouped weight gradients (bf16): the split-K partials and column-sum
+  // partials of a layer's four products, and their split counts
+  int64_t gpart = -1, gcs = -1;
+  int gsplit[4] = {1, 1, 1, 1};
   int64_t normpart;
   int64_t ska, sva, skb, svb, seg, nseg;
   int64_t flags, scale, norm;
@@ -181,6 +190,7 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
   P.loss_tmp = take(4);
   P.dres = take(4 * M * C);
   P.dres_lp = prec == GPT2_BF16 ? take(a * M * C) : P.dres;
+  if (prec == GPT2_BF16) P.dres_lp2 = take(a * M * C);
   P.dh = take(a * M * C);
   P.datty = take(a * M * C);
   P.dqkv = take(a * M * 3 * C);
@@ -206,7 +216,19 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
     P.wpart[k] = P.split[k] > 1 ? take(4 * (int64_t)P.split[k] * wsz[k]) : 0;
     P.cspart[k] = take(4 * (int64_t)P.split[k] * wout[k]);
   }
-  for (int k = 0; k < 4; k++) P.lnpart[k] = take(4 * (int64_t)layernorm_bwd_parts((int)M) * 2 * C);
+  for (int k = 0; k < 5; k++) P.lnpart[k] = take(4 * (int64_t)layernorm_bwd_parts((int)M) * 2 * C);
+  if (prec == GPT2_BF16) {
+    const int gt = gemm_group_tiles(3 * Ci, Ci) + gemm_group_tiles(Ci, Ci) + gemm_group_tiles(4 * Ci, Ci) +
+                   gemm_group_tiles(Ci, 4 * Ci);
+    int64_t wp = 0, cp = 0;
+    for (int k = 0; k < 4; k++) {
+      P.gsplit[k] = gemm_group_split_hint((int)wout[k], (int)(wsz[k] / wout[k]), Mi, gt);
+      if (P.gsplit[k] > 1) wp += (int64_t)P.gsplit[k] * wsz[k];
+      cp += (int64_t)P.gsplit[k] * wout[k];
+    }
+    P.gpart = take(4 * std::max<int64_t>(wp, 1));
+    P.gcs = take(4 * cp);
+  }
   if (fp8) {
     P.w8 = take(make_layout(c).total);
     P.wsc = take(4 * ((int64_t)c.padded_vocab_size + L * 9 * C));  // rows of wte and the four per-layer matrices
@@ -260,6 +282,10 @@ struct gpt2_handle {
   // ev_done[5]: the tied head's weight gradient there; ev_done[6]: a layer's
   // batched reduction of partial sums there
   hipEvent_t ev_fork = nullptr, ev_done[7] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+  // grouped weight gradients (bf16): a layer's section on the second stream,
+  // one event per layer parity (the main stream waits for the layer above's
+  // while the current layer's may still be running)
+  hipEvent_t ev_layer[2] = {nullptr, nullptr};
   Layout lay;
   Plan plan;
   std::vector<const Tensor*> by_kind_layer;  // [kind * (L+1) + layer+1]
@@ -473,6 +499,61 @@ int weight_grad(gpt2_t* h, const void* dY, const void* X, int N, int K, float* d
   return rc;
 }
 
+// A layer's four weight gradients (qkv, attention projection, MLP up and
+// down; each dW (+)= dY^T X with its bias gradient as fused column sums) in
+// one grouped launch.  Products with more than one split leave fp32 partials
+// that are reduced in order into the gradients with the layer's other
+// partial sums.
+struct WGrad {
+  const void* dY;
+  const void* X;
+  int N, K;  // dW is [N, K]
+  float *dW, *db;
+};
+
+int weight_grad_group(gpt2_t* h, const WGrad (&w)[4], int accumulate) {
+  const Plan& P = h->plan;
+  GemmArgs g[4];
+  int64_t wp = 0, cp = 0;
+  for (int k = 0; k < 4; k++) {
+    GemmArgs& a = g[k];
+    a.A = w[k].dY;
+    a.lda = w[k].N;
+    a.B = w[k].X;
+    a.ldb = w[k].K;
+    a.M = w[k].N;
+    a.N = w[k].K;
+    a.K = (int)h->M;
+    a.splits = P.gsplit[k];
+    a.ldc = w[k].K;
+    a.colsum = h->w<float>(P.gcs) + cp;
+    a.colsum_stride = w[k].N;
+    cp += (int64_t)a.splits * w[k].N;
+    if (a.splits == 1) {
+      a.C = w[k].dW;
+      a.accumulate = accumulate;
+    } else {
+      a.C = h->w<float>(P.gpart) + wp;
+      a.split_stride = (int64_t)w[k].N * w[k].K;
+      wp += (int64_t)a.splits * w[k].N * w[k].K;
+    }
+  }
+  double fl = 0;
+  for (auto& a : g) fl += 2.0 * a.M * a.N * a.K;
+  Timer t(h, K_GEMM_TN_F32, fl);
+  hipError_t e = gemm_group(h->st, g, 4);
+  t.done();
+  int rc = hip_check(h, e, "weight gradients");
+  if (rc) return rc;
+  for (int k = 0; k < 4; k++) {
+    if (g[k].splits > 1)
+      queue_reduction(h, static_cast<const float*>(g[k].C), g[k].splits, g[k].split_stride, w[k].dW, w[k].N * w[k].K,
+                      accumulate);
+    queue_reduction(h, g[k].colsum, g[k].splits, w[k].N, w[k].db, w[k].N, accumulate);
+  }
+  return GPT2_OK;
+}
+
 // The main stream waits for the second-stream work that recorded ev_done[ev]
 // (and, by that stream's order, for everything enqueued there before it).
 int join_side(gpt2_t* h, int ev) {
@@ -498,10 +579,11 @@ class SideSection {
     if (!rc) h_->st = h_->side;
     return rc;
   }
-  int close(int ev) {
+  int close(int ev) { return close_event(h_->ev_done[ev]); }
+  int close_event(hipEvent_t e) {
     h_->st = saved_;
     if (!h_->overlap) return GPT2_OK;
-    return hip_check(h_, hipEventRecord(h_->ev_done[ev], h_->side), "side done");
+    return hip_check(h_, hipEventRecord(e, h_->side), "side done");
   }
 
  private:
@@ -650,6 +732,11 @@ int gpt2_init(gpt2_t** out, const gpt2_config_t* cfg, int precision, int B, int 
       gpt2_destroy(h);
       return GPT2_ERR_HIP;
     }
+  for (auto& e : h->ev_layer)
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence) != hipSuccess) {
+      gpt2_destroy(h);
+      return GPT2_ERR_HIP;
+    }
   *out = h;
   return GPT2_OK;
 }
@@ -666,6 +753,8 @@ void gpt2_destroy(gpt2_t* h) {
   }
   if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
   for (auto& e : h->ev_done)
+    if (e) (void)hipEventDestroy(e);
+  for (auto& e : h->ev_layer)
     if (e) (void)hipEventDestroy(e);
   delete h;
 }
@@ -881,9 +970,82 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
   GemmArgs g = dx_args(h, h->w<void>(P.logits), h->W(T_WTE), Vp, C, h->w<void>(P.dh));
   g.alpha = alpha;
   if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "lm_head dx"))) return rc;
+  // grouped weight gradients (bf16 without activation recompute): the matmul
+  // copy of a layer's block-output gradient alternates between two buffers
+  const bool grouped = lp && !h->recompute;
+  auto dres_lp_slot = [&](int layer) { return grouped && (layer & 1) ? P.dres_lp2 : P.dres_lp; };
   if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[L]), h->w<float>(P.meanf), h->w<float>(P.rstdf), T_LNFG,
-                        -1, 0, P.dres_lp, 0, acc)))
+                        -1, 0, dres_lp_slot(L - 1), 0, acc)))
     return rc;
+
+  if (grouped) {
+    // Per layer, on the main stream: the input gradients, LayerNorm and
+    // attention backward.  After the attention backward the layer's four
+    // weight gradients go to the second stream as one grouped launch, behind
+    // the queued reductions of the layer above.  Everything such a launch
+    // reads alternates between two buffers by layer (the block-output
+    // gradient's matmul copy, du, LayerNorm 2's copy, dqkv; also the
+    // LayerNorm partial sums its section reduces), so the main stream waits
+    // for layer l+1's section only before LayerNorm 1 of layer l rewrites the
+    // buffer that section read.
+    for (int l = L - 1; l >= 0; l--) {
+      void* dres_op_l = h->w<void>(dres_lp_slot(l));
+      void* du = h->w<void>((l & 1) ? P.du2 : P.du);
+      void* dqkv = h->w<void>((l & 1) ? P.dqkv2 : P.dqkv);
+      const int64_t lp2_off = P.lp2[l & 1];
+      void* ln2_op = h->w<void>(lp2_off);
+      g = dx_args(h, dres_op_l, h->W(T_FCPW, l), C, 4 * C, du);
+      g.aux = h->w<void>(P.u[l]);
+      g.ldaux = 4 * C;
+      if ((rc = run_gemm(h, K_GEMM_NN_GELU_BWD, 0, 1, EPI_GELU_BWD, g, "fcproj dx"))) return rc;
+      g = dx_args(h, du, h->W(T_FCW, l), 4 * C, C, h->w<void>(P.dh));
+      if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "fc dx"))) return rc;
+      if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_mid[l]), h->w<float>(P.mean2[l]),
+                            h->w<float>(P.rstd2[l]), T_LN2G, l, 1 + (l & 1), lp2_off, 1, acc)))
+        return rc;
+      g = dx_args(h, ln2_op, h->W(T_PROJW, l), C, C, h->w<void>(P.datty));
+      if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "proj dx"))) return rc;
+      {
+        const double pairs = (double)h->B * NH * ((double)h->T * (h->T + 1) / 2);
+        {
+          Timer t(h, K_ATTN_DQ, 4.0 * hd * pairs);
+          rc = hip_check(h, attn_bwd_dq(h->st, h->prec, h->w<void>(P.qkv[l]), h->w<void>(P.atty[l]),
+                                        h->w<void>(P.datty), h->w<float>(P.lse[l]), h->w<float>(P.dsum), dqkv, h->B,
+                                        h->T, NH, hd),
+                         "attn dq");
+        }
+        if (rc) return rc;
+        {
+          Timer t(h, K_ATTN_DKV, 4.0 * hd * pairs);
+          rc = hip_check(h, attn_bwd_dkv(h->st, h->prec, h->w<void>(P.qkv[l]), h->w<void>(P.datty),
+                                         h->w<float>(P.lse[l]), h->w<float>(P.dsum), dqkv, h->B, h->T, NH, hd),
+                         "attn dkv");
+        }
+        if (rc) return rc;
+      }
+      {
+        SideSection side(h);
+        if ((rc = side.open())) return rc;
+        rc = flush_reductions(h);  // the layer above's partial sums (and this layer's LayerNorm 2's)
+        const WGrad w[4] = {{dqkv, h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l), h->G32(T_QKVB, l)},
+                            {ln2_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l)},
+                            {du, h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), h->G32(T_FCB, l)},
+                            {dres_op_l, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l)}};
+        if (!rc) rc = weight_grad_group(h, w, acc);
+        if (rc || (rc = side.close_event(h->ev_layer[l & 1]))) return rc;
+      }
+      g = dx_args(h, dqkv, h->W(T_QKVW, l), 3 * C, C, h->w<void>(P.dh));
+      if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "qkv dx"))) return rc;
+      // LayerNorm 1 writes the block-output gradient's copy for layer l-1,
+      // the buffer layer l+1's weight gradients read
+      if (l < L - 1 && h->overlap &&
+          (rc = hip_check(h, hipStreamWaitEvent(h->st, h->ev_layer[(l + 1) & 1], 0), "join wait")))
+        return rc;
+      if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[l]), h->w<float>(P.mean1[l]),
+                            h->w<float>(P.rstd1[l]), T_LN1G, l, 3 + (l & 1), dres_lp_slot(l - 1), 1, acc)))
+        return rc;
+    }
+  } else {
 
   // Second stream, per layer: one section before the MLP down-projection's
   // input gradient (the layer above's queued reductions, then this
@@ -987,6 +1149,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
                           T_LN1G, l, 3, P.dres_lp, 1, acc)))
       return rc;
   }
+  }  // grouped
   // layer 0's partial sums (the last layer processed), on the second stream
   // behind its products
   {

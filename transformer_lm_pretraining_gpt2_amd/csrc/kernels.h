@@ -49,6 +49,19 @@ struct GemmArgs {
 };
 
 hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArgs& g);
+// Up to kMaxGemmGroup weight-gradient products (a_t = b_t = 1, EPI_F32, bf16,
+// each with its own splits and optional column sums) in one launch.
+constexpr int kMaxGemmGroup = 4;
+struct GemmGroup {
+  GemmArgs p[kMaxGemmGroup];
+  int block0[kMaxGemmGroup + 1];  // filled in by gemm_group
+  int count;
+};
+hipError_t gemm_group(hipStream_t st, const GemmArgs* probs, int count);
+// split-K factor of a product inside a group of products whose output tiles
+// total `group_tiles` (one round of blocks over the chip)
+int gemm_group_split_hint(int M, int N, int K, int group_tiles);
+int gemm_group_tiles(int M, int N);
 // forward product (a_t = b_t = 0) with FP8 E4M3 operands A, B (bytes) and
 // bf16 / fp32 outputs as in gemm; acc(i, j) is multiplied by scale_a[i] * scale_b[j]
 hipError_t gemm_fp8(hipStream_t st, int epi, const GemmArgs& g);
