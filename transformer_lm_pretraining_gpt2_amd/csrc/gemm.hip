@@ -951,12 +951,16 @@ hipError_t launch(hipStream_t st, const GemmArgs& g) {
 //    reduction-contiguous), where it saves the staging registers.  Its single
 //    tile of look-ahead is too short for the tied head's long sweep.
 //  * TILE_P256_W8 / TILE_P192_W8: the persistent versions of the two 8-wave
-//    tiles (gemm_persist_kernel) for products with more than one round of
-//    tiles (more tiles than CUs) and an even number of reduction steps: at
-//    124M the qkv and tied-head forward products and the MLP's input
-//    gradient (66 vs 70 us, 1347 vs 1487 us, 92 vs 104 us, interleaved runs
-//    on one box).  The 256x192 tile also serves the MLP input gradient, whose
-//    GELU' epilogue spills registers on the 256x256 one.
+//    tiles (gemm_persist_kernel) for forward products with more than one
+//    round of tiles (more tiles than CUs) and an even number of reduction
+//    steps: at 124M the qkv and tied-head forward products (66 vs 70 us and
+//    1347 vs 1487 us, interleaved runs on one box).  Input-gradient products
+//    stay per-tile: they run beside the second stream's weight gradients,
+//    and a persistent block that lands on a busy CU holds up its whole tile
+//    sequence (MLP input gradient persistent: 92 us alone but 220 us in the
+//    step; the step 18.53 -> 18.32 ms without it).  The 256x192 tile also
+//    serves the MLP input gradient, whose GELU' epilogue spills registers on
+//    the 256x256 one.
 enum TileKind {
   TILE_128 = 0, TILE_128_K32, TILE_256x192_K32, TILE_256_W8, TILE_256_W8_K32, TILE_D256_W8, TILE_192_W8,
   TILE_P256_W8, TILE_P192_W8
@@ -971,7 +975,7 @@ TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
   // 192-wide outputs: the model-width products, the qkv projection, and the
   // MLP's input gradient (whose GELU' epilogue spills on the 256-wide tile)
   if (N % 192 == 0 && (N <= 2304 || b_t) && mn >= 4000000)
-    return !a_t && even && rounds(192) ? TILE_P192_W8 : TILE_192_W8;
+    return !a_t && !b_t && even && rounds(192) ? TILE_P192_W8 : TILE_192_W8;
   if (K >= 2048 || mn >= 40000000) {
     if (!a_t && !b_t && N <= 4096) return TILE_D256_W8;
     return !a_t && !b_t && even && rounds(256) ? TILE_P256_W8 : TILE_256_W8;
