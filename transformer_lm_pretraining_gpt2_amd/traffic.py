@@ -23,11 +23,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # the GPT-2 124M bf16 workload, most workgroups per launch or None); a launch
 # of any of them counts as one launch
 KERNELS = {
-    # weight gradients of the four per-layer linears: the 8-wave 256x256 tile,
-    # BK = 32, split over the reduction into one round of at most one block
-    # per CU; the tied head's weight gradient (591 blocks) shares the
-    # instantiation and is left out by its size
-    "gemm_tn_f32": (["gemm_kernelIDF16bLi256ELi256ELi32ELi2ELi4ELi1ELi1ELi4E"], 256),
+    # a layer's four weight gradients in one grouped launch: the 8-wave 256x256
+    # tile, BK = 32, each product split over the reduction so the group makes
+    # one round of at most one block per CU (the tied head's weight gradient
+    # is a separate, ungrouped kernel)
+    "gemm_tn_f32": (["gemm_group_kernelIDF16bLi256ELi256ELi32ELi2ELi4ELi1ELi1ELi4E"], None),
     "attn_bwd_dkv": (["attn_dkv_kernelIDF16bLi64E"], None),
 }
 COPY = "copyBuffer"  # the runtime's device-to-device copy kernel, used by dst.copy_(src)
