@@ -91,16 +91,17 @@ def batches(model, B, T, K, seed, data="zipf", index0=0):
 # terms errs by about sqrt(2) * 2.4 % = 3.4 % of its RMS.  Every gradient
 # passes through several such products and 12 layers of FP8 forward
 # activations, so per-tensor gradients land some 5-10 % from the exact ones
-# (measured 6 % at 4 layers, 8.6 % at 124M); the bar is 0.2, well below the
-# 100 % of a dropped scale or a transposed operand.  The loss moves by the
-# logits' perturbation (measured 2e-3 to 6e-3): bar 5e-2.
+# (measured against the oracle: 6 % at 4 layers, 8.7 % at 124M, 9.2 % at 350M;
+# against the bf16 path on the same inputs: 8.7 % at 124M); the bar is 0.15,
+# well below the 100 % of a dropped scale or a transposed operand.  The loss
+# moves by the logits' perturbation (measured 1e-3 to 6e-3): bar 5e-2.
 # The per-position FP8 losses carry the logits' perturbation, which every
 # layer's four FP8 products feed with independent rounding noise: its RMS grows
 # as sqrt(n_layer), so the per-position bar is 0.2 at 12 layers, scaled by
 # sqrt(n_layer / 12) (0.28 for the 24-layer 350M model).
 TOL = {"fp32": dict(loss=1e-4, grad=1e-4, param=1e-4, rows=1e-4),
        "bf16": dict(loss=2e-2, grad=3e-2, param=3e-2, rows=1e-1),
-       "fp8": dict(loss=5e-2, grad=2e-1, param=5e-2, rows=2e-1)}
+       "fp8": dict(loss=5e-2, grad=1.5e-1, param=5e-2, rows=2e-1)}
 
 
 def rows_bar(model, prec):
