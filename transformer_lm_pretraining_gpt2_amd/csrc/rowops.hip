@@ -246,8 +246,11 @@ __global__ void __launch_bounds__(RED_THREADS) reduce_jobs_kernel(ReduceJobs job
     const int64_t j = ((int64_t)blk * CH + c) * 4;
     const int p0 = (int)((int64_t)J.nparts * slice / RED_SLICES), p1 = (int)((int64_t)J.nparts * (slice + 1) / RED_SLICES);
     f32x4 t = {0.f, 0.f, 0.f, 0.f};
-    if (j < J.n)
+    // (unrolled so eight loads are in flight; the additions keep their order)
+    if (j < J.n) {
+#pragma unroll 8
       for (int p = p0; p < p1; p++) t += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(J.part + (int64_t)p * J.ld + j));
+    }
     sh[tid] = t;
     __syncthreads();
     if (slice == 0 && j < J.n) {
