@@ -62,10 +62,11 @@ typedef enum { GPT2_FP32 = 0, GPT2_BF16 = 1 } gpt2_precision_t;
  * activation recompute for the MLP (llm.c's -r option, "Reproducing GPT-2
  * (124M) cheaply with llm.c", training command flags).  Each layer keeps only
  * the MLP pre-activation (in the activation type) instead of GELU' and the
- * GELU output; one GELU-output buffer serves all layers and gpt2_backward
- * rebuilds it from the pre-activation before each layer's MLP weight
- * gradient.  The workspace shrinks by (n_layer - 1) * B * T * 4 * n_embd
- * activation elements; the step costs one extra elementwise pass per layer.
+ * GELU output; two GELU-output buffers serve all layers (by layer parity) and
+ * gpt2_backward rebuilds a layer's from the pre-activation before its MLP
+ * weight gradient.  The workspace shrinks by (n_layer - 2) * B * T * 4 *
+ * n_embd activation elements (n_layer >= 2); the step costs one extra
+ * elementwise pass per layer.
  * The activation is taken from the rounded pre-activation in this mode, so
  * bf16 results differ from the default mode within rounding (fp32 results
  * are identical). */

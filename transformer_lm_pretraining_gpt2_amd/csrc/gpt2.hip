@@ -179,8 +179,10 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
     P.atty.push_back(take(a * M * C));
     P.lse.push_back(take(4 * M * NH));
     P.u.push_back(take(a * M * 4 * C));
-    // with activation recompute every layer's GELU output shares layer 0's buffer
-    P.g.push_back(recompute && l > 0 ? P.g[0] : take(a * M * 4 * C));
+    // with activation recompute the layers' GELU outputs share two buffers,
+    // by layer parity (a layer's weight gradients may still read one while
+    // the next layer down rebuilds the other)
+    P.g.push_back(recompute && l > 1 ? P.g[l & 1] : take(a * M * 4 * C));
   }
   P.hf = take(a * M * C);
   P.meanf = take(4 * M);
@@ -273,7 +275,7 @@ struct gpt2_handle {
   // or reads their partial sums.
   hipStream_t side = nullptr;
   bool overlap = true;
-  bool recompute = false;  // GPT2_RECOMPUTE_GELU: the layers share one GELU-output buffer
+  bool recompute = false;  // GPT2_RECOMPUTE_GELU: the layers share two GELU-output buffers
   bool fp8 = false;        // GPT2_FP8_FWD: forward products on FP8 copies
   std::vector<QuantJob> wquant;     // the weights' FP8 copies, one job per matrix
   std::vector<int64_t> wsc_off;     // [kind * (L+1) + layer+1]: row-scale offset (floats) in plan.wsc
@@ -970,9 +972,9 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
   GemmArgs g = dx_args(h, h->w<void>(P.logits), h->W(T_WTE), Vp, C, h->w<void>(P.dh));
   g.alpha = alpha;
   if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "lm_head dx"))) return rc;
-  // grouped weight gradients (bf16 without activation recompute): the matmul
-  // copy of a layer's block-output gradient alternates between two buffers
-  const bool grouped = lp && !h->recompute;
+  // grouped weight gradients (bf16): the matmul copy of a layer's
+  // block-output gradient alternates between two buffers
+  const bool grouped = lp;
   auto dres_lp_slot = [&](int layer) { return grouped && (layer & 1) ? P.dres_lp2 : P.dres_lp; };
   if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_in[L]), h->w<float>(P.meanf), h->w<float>(P.rstdf), T_LNFG,
                         -1, 0, dres_lp_slot(L - 1), 0, acc)))
@@ -989,6 +991,15 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     // for layer l+1's section only before LayerNorm 1 of layer l rewrites the
     // buffer that section read.
     for (int l = L - 1; l >= 0; l--) {
+      // activation recompute: rebuild this layer's GELU output (the last
+      // two layers' are still in their buffers from the forward); the
+      // buffer's previous reader, layer l+2's weight gradients, was joined
+      // before LayerNorm 1 of layer l+1
+      if (h->recompute && l < L - 2) {
+        rc = hip_check(h, gelu_fwd(h->st, h->prec, h->w<void>(P.u[l]), h->w<void>(P.g[l]), h->M * 4 * C),
+                       "gelu recompute");
+        if (rc) return rc;
+      }
       void* dres_op_l = h->w<void>(dres_lp_slot(l));
       void* du = h->w<void>((l & 1) ? P.du2 : P.du);
       void* dqkv = h->w<void>((l & 1) ? P.dqkv2 : P.dqkv);
@@ -997,6 +1008,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
       g = dx_args(h, dres_op_l, h->W(T_FCPW, l), C, 4 * C, du);
       g.aux = h->w<void>(P.u[l]);
       g.ldaux = 4 * C;
+      g.preact = h->recompute;
       if ((rc = run_gemm(h, K_GEMM_NN_GELU_BWD, 0, 1, EPI_GELU_BWD, g, "fcproj dx"))) return rc;
       g = dx_args(h, du, h->W(T_FCW, l), 4 * C, C, h->w<void>(P.dh));
       if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "fc dx"))) return rc;
@@ -1064,11 +1076,11 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     void* dqkv = h->w<void>((l & 1) ? P.dqkv2 : P.dqkv);
     const int64_t lp2_off = P.lp2[l & 1];
     void* ln2_op = lp ? h->w<void>(lp2_off) : dres;  // matmul view of dres after LayerNorm 2
-    // activation recompute: rebuild this layer's GELU output in the shared
-    // buffer (the last layer's is still there from the forward); its reader
-    // in the layer above (the fcproj weight gradient) was joined before that
-    // layer's LayerNorm 1 backward
-    if (h->recompute && l < L - 1) {
+    // activation recompute: rebuild this layer's GELU output in its shared
+    // buffer (the last two layers' are still there from the forward); its
+    // reader two layers above (the fcproj weight gradient) was joined before
+    // the layer above's LayerNorm 1 backward
+    if (h->recompute && l < L - 2) {
       rc = hip_check(h, gelu_fwd(h->st, h->prec, h->w<void>(P.u[l]), h->w<void>(P.g[l]), h->M * 4 * C), "gelu recompute");
       if (rc) return rc;
     }
