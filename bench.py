@@ -131,6 +131,8 @@ def main():
                     help="forward products on FP8 E4M3 copies (per-row scales); reported as its own dtype")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the whole step on one stream (no second stream for the weight gradients)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each micro-step's forward + backward from a captured HIP graph (AdamW eager)")
     ap.add_argument("--mode", choices=["train", "eval"], default="train",
                     help="eval: forward-only validation loss over held-out batches instead of the training step")
     args = ap.parse_args()
@@ -179,11 +181,33 @@ def main():
     loss = torch.zeros(1, device=dev)
     norm = torch.zeros(1, device=dev)
 
-    def one_step(s):
+    graphs = {}
+    if args.graph:
+        # One graph per kind of micro-step (the first overwrites the
+        # gradients, later ones add), captured on torch's capture stream; the
+        # graphs read the micro-batch from fixed buffers, refilled before each
+        # replay.  Capturing enqueues nothing.
+        g_ids = torch.empty(B * T, dtype=torch.int32, device=dev)
+        g_tgt = torch.empty(B * T, dtype=torch.int32, device=dev)
+        home = step.stream
+        for acc in ((0, 1) if K > 1 else (0,)):
+            graphs[acc] = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graphs[acc]):
+                step.set_stream(torch.cuda.current_stream())
+                step.forward(g_ids, g_tgt, loss)
+                step.backward(acc, K)
+            step.set_stream(home)
+
+    def one_step(s, graph=False):
         for k in range(K):
             i = s * K + k
-            step.forward(d_ids[i], d_tgt[i], loss)
-            step.backward(k, K)
+            if graph:
+                g_ids.copy_(d_ids[i])
+                g_tgt.copy_(d_tgt[i])
+                graphs[min(k, 1)].replay()
+            else:
+                step.forward(d_ids[i], d_tgt[i], loss)
+                step.backward(k, K)
         step.adamw_step(s + 1, lr_at(s, rc.max_lr, rc.warmup, rc.max_steps), rc.beta1, rc.beta2, rc.eps,
                         rc.weight_decay, rc.grad_clip, norm)
 
@@ -196,7 +220,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     for s in range(W):
-        one_step(s)
+        one_step(s, args.graph)
     st = step.sync_status()
     if st != 0:
         raise SystemExit(f"warmup step failed: {binding.ERRORS.get(st, st)}")
@@ -209,7 +233,7 @@ def main():
     t0 = time.perf_counter()
     evs[0].record()
     for j, s in enumerate(range(W, W + S)):
-        one_step(s)
+        one_step(s, args.graph)
         evs[j + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -292,7 +316,7 @@ def main():
                                f"->{model.padded_vocab_size}",
                    "global_batch": B * K, "seq_len": T, "grad_accum": K, "parallelism": "none (1 GPU)",
                    "activation_recompute": bool(args.recompute), "fp8_forward": bool(args.fp8),
-                   "two_streams": not args.no_overlap,
+                   "two_streams": not args.no_overlap, "hip_graph": bool(args.graph),
                    "workspace_bytes": int(step.workspace.numel())},
         "roofline": roof,
         "loss_first_timed": round(first_loss, 4),

@@ -154,7 +154,18 @@ void gpt2_destroy(gpt2_t* h);
  * (needed once after the caller fills params; AdamW keeps it current). */
 int gpt2_refresh_params(gpt2_t* h);
 
-/* Replaces the stream later calls enqueue on. */
+/* Replaces the stream later calls enqueue on.
+ *
+ * Graph capture: gpt2_forward, gpt2_eval and gpt2_backward enqueue kernels
+ * and event records/waits only (no allocation, memset, copy or host
+ * synchronisation), so a caller may capture one micro-step into a HIP graph
+ * by setting its capturing stream here first: the handle's second stream
+ * joins the capture through an event recorded on that stream and is joined
+ * back before each call returns.  A graph freezes the call's arguments (the
+ * input and loss pointers, micro_step > 0 or not); replays read whatever the
+ * caller's input buffers hold then.  gpt2_adamw_step takes the step and
+ * learning rate by value, so it stays outside a graph replayed over steps.
+ * Set the stream back to the one replays and later calls use afterwards. */
 int gpt2_set_stream(gpt2_t* h, void* stream);
 
 /* Overlap (default on): gpt2_backward runs the tied head's and each layer's

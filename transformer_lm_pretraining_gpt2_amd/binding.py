@@ -237,6 +237,11 @@ class TrainStep:
         """Returns the deferred status code (0 = ok) after synchronising."""
         return int(lib().gpt2_sync_status(self.h))
 
+    def set_stream(self, stream):
+        """Stream later calls enqueue on (a torch.cuda.Stream)."""
+        self._check(lib().gpt2_set_stream(self.h, stream.cuda_stream), "set_stream")
+        self.stream = stream
+
     def set_overlap(self, enable=True):
         """Weight-gradient products on the handle's second stream (default) or all on one stream."""
         self._check(lib().gpt2_set_overlap(self.h, 1 if enable else 0), "set_overlap")
