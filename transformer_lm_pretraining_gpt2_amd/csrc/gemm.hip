@@ -91,6 +91,26 @@ struct Operand {
       *reinterpret_cast<f32x4*>(s + gr * LD + gc * VE) = reg[c];
     }
   }
+  // Strided operands (TRANS = 1): every chunk a thread stages covers the same
+  // VE operand rows (NT is a multiple of the chunks per reduction row), so
+  // the thread can keep per-row sums of the reduction values it stages,
+  // chunk by chunk in reduction order.  w is 1 (or 0 for a staged re-read
+  // past the last step: a multiply, not a branch, which would split the main
+  // loop and cost register copies).
+  __device__ __forceinline__ void row_sums(float (&acc)[VE], float w) const {
+    static_assert(TRANS == 1 && NT % CPR == 0, "row sums need a fixed row range per thread");
+#pragma unroll
+    for (int c = 0; c < PER; c++) {
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, reg[c]);
+#pragma unroll
+        for (int e = 0; e < VE; e++) acc[e] = __builtin_fmaf((float)v[e], w, acc[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < VE; e++) acc[e] = __builtin_fmaf(reg[c][e], w, acc[e]);
+      }
+    }
+  }
   // part p of NP of the store (chunks spread over the substeps of a tile)
   template <int NP>
   __device__ __forceinline__ void store_part(T* s, int tid, int p) const {
@@ -542,9 +562,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split
   // of substep ks+1 are read before the MFMAs of substep ks are issued, so LDS
   // latency overlaps the matrix core (a gain when both operands come from
   // plain LDS rows; with two transposed operands the extra registers cost
-  // more than the overlap wins).  CSV = 1 also accumulates the bias gradient
-  // sum_r A(i, r) from the A fragments: each lane adds its 8 reduction values
-  // per fragment in a fixed order.
+  // more than the overlap wins).  GEMM_MAINLOOP(1) also accumulates the bias
+  // gradient sum_r A(i, r) from the staged A chunks (Operand::row_sums).
   constexpr bool PIPE = AT == 0 && !FP8;  // (FP8 fragments are twice as wide: no room for a second set)
   // With BK = 64 (four substeps per tile) the next tile's LDS stores are
   // spread over the substeps, overlapping them with the MFMAs (they fill the
@@ -555,9 +574,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split
 #define GEMM_FRAGS(AS, BS, KS, FA, FB)                                                            \
   _Pragma("unroll") for (int ti = 0; ti < TI; ti++) FA[ti] = OA::frag(AS, wi * WTI + ti * 32, KS, lane); \
   _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) FB[tj] = OB::frag(BS, wj * WTJ + tj * 32, KS, lane);
-#define GEMM_COMPUTE(AS, BS, CSV, PP) GEMM_COMPUTE_ST(AS, BS, CSV, PP, (void)0)
+#define GEMM_COMPUTE(AS, BS, PP) GEMM_COMPUTE_ST(AS, BS, PP, (void)0)
   // ST(ks): work interleaved with substep ks (the next tile's LDS stores)
-#define GEMM_COMPUTE_ST(AS, BS, CSV, PP, ST)                                                      \
+#define GEMM_COMPUTE_ST(AS, BS, PP, ST)                                                           \
   {                                                                                               \
     FI fa[2][TI], fb[2][TJ];                                                                      \
     if constexpr (PP) { GEMM_FRAGS(AS, BS, 0, fa[0], fb[0]) }                                     \
@@ -568,9 +587,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split
         if (ks + 1 < NSUB) { GEMM_FRAGS(AS, BS, ks + 1, fa[cur ^ 1], fb[cur ^ 1]) }            \
       } else {                                                                                    \
         GEMM_FRAGS(AS, BS, ks, fa[0], fb[0])                                                      \
-      }                                                                                           \
-      if constexpr (CSV) {                                                                        \
-        _Pragma("unroll") for (int ti = 0; ti < TI; ti++) cs[ti] = frag_sum(fa[cur][ti], cs[ti]); \
       }                                                                                           \
       _Pragma("unroll") for (int ti = 0; ti < TI; ti++)                                           \
         _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) mma16(acc[ti][tj], fb[cur][tj], fa[cur][ti]); \
@@ -598,6 +614,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split
     b1.load(min(kbeg + BK, klast));                                                               \
     a0.store(sA[0], tid);                                                                         \
     b0.store(sB[0], tid);                                                                         \
+    if constexpr (CSV) a0.row_sums(rs, 1.f);                                                      \
     __syncthreads();                                                                              \
     for (int kt = 0; kt + 2 <= nk; kt += 2) {                                                     \
       /* buffer 0 holds tile kt, registers 1 hold tile kt+1 */                                    \
@@ -605,31 +622,33 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split
       a0.load(k2);                                                                                \
       b0.load(k2);                                                                                \
       if constexpr (ILV) {                                                                        \
-        GEMM_COMPUTE_ST(sA[0], sB[0], CSV, PIPE,                                                  \
+        GEMM_COMPUTE_ST(sA[0], sB[0], PIPE,                                                  \
                         (a1.template store_part<NSUB>(sA[1], tid, ks),                         \
                          b1.template store_part<NSUB>(sB[1], tid, ks)))                        \
       } else {                                                                                    \
-        GEMM_COMPUTE(sA[0], sB[0], CSV, PIPE)                                                     \
+        GEMM_COMPUTE(sA[0], sB[0], PIPE)                                                     \
         a1.store(sA[1], tid);                                                                     \
         b1.store(sB[1], tid);                                                                     \
       }                                                                                           \
+      if constexpr (CSV) a1.row_sums(rs, 1.f); /* tile kt+1 (kt + 2 <= nk) */                    \
       __syncthreads();                                                                            \
       /* buffer 1 holds tile kt+1, registers 0 hold tile kt+2 */                                  \
       a1.load(k3);                                                                                \
       b1.load(k3);                                                                                \
       if constexpr (ILV) {                                                                        \
-        GEMM_COMPUTE_ST(sA[1], sB[1], CSV, PIPE,                                                  \
+        GEMM_COMPUTE_ST(sA[1], sB[1], PIPE,                                                  \
                         (a0.template store_part<NSUB>(sA[0], tid, ks),                         \
                          b0.template store_part<NSUB>(sB[0], tid, ks)))                        \
       } else {                                                                                    \
-        GEMM_COMPUTE(sA[1], sB[1], CSV, PIPE)                                                     \
+        GEMM_COMPUTE(sA[1], sB[1], PIPE)                                                     \
         a0.store(sA[0], tid);                                                                     \
         b0.store(sB[0], tid);                                                                     \
       }                                                                                           \
+      if constexpr (CSV) a0.row_sums(rs, kt + 2 < nk ? 1.f : 0.f); /* tile kt+2, if any */       \
       __syncthreads();                                                                            \
     }                                                                                             \
     if (nk & 1) { /* the last tile sits in buffer 0 (no read-ahead: registers are tight here) */  \
-      GEMM_COMPUTE(sA[0], sB[0], CSV, false)                                                      \
+      GEMM_COMPUTE(sA[0], sB[0], false)                                                      \
     }                                                                                             \
   }
 
@@ -663,7 +682,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split
         GEMM_DFRAGS(nxt, 0, fa[c ^ 1], fb[c ^ 1])                                                         \
       }                                                                                                   \
       if constexpr (CSV) {                                                                                \
-        _Pragma("unroll") for (int ti = 0; ti < TI; ti++) cs[ti] = frag_sum(fa[c][ti], cs[ti]);           \
+        _Pragma("unroll") for (int ti = 0; ti < TI; ti++)                                                 \
+          if (ti % WJ == wj) cs[ti] = frag_sum(fa[c][ti], cs[ti]);                                        \
       }                                                                                                   \
       _Pragma("unroll") for (int ti = 0; ti < TI; ti++)                                                   \
         _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) mma16(acc[ti][tj], fb[c][tj], fa[c][ti]);       \
@@ -693,14 +713,22 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split
     GEMM_DTL_TILE(CSV, true)                                                                              \
   }
 
-  // Only the blocks of the first column tile (bj == 0) sum the bias gradient
-  // (and of those only the waves with wj == 0 write it).  The choice is made
-  // once per block, outside the main loop, so the loop itself stays one
-  // branch-free block and every wave passes the same barriers.
+  // Only the blocks of the first column tile (bj == 0) sum the bias gradient.
+  // The choice is made once per block, outside the main loop, so the loop
+  // itself stays one branch-free block and every wave passes the same
+  // barriers.  On the register path each thread sums the A chunks it stages
+  // (no dependence on the LDS fragment reads, which the MFMAs wait for; sums
+  // of the fragments held the MFMAs back and made the summing blocks a fifth
+  // slower than the others, which set the time of a weight-gradient launch);
+  // the direct-to-LDS path sums fragments, each wave column a share of the
+  // rows.
   const bool do_cs = HAS_CS && g.colsum != nullptr && bj == 0;
-  float cs[TI];
+  float cs[TI];  // direct-to-LDS path: sums of the A fragments
 #pragma unroll
   for (int ti = 0; ti < TI; ti++) cs[ti] = 0.f;
+  float rs[OA::VE];  // register path: sums of the staged A chunks
+#pragma unroll
+  for (int e = 0; e < OA::VE; e++) rs[e] = 0.f;
   if constexpr (NBUF > 0) {
     static_assert(sizeof(T) == 2 && BK % 32 == 0, "direct-to-LDS loads: bf16, even substep count");
     if constexpr (HAS_CS) {
@@ -718,12 +746,33 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split
 #undef GEMM_DTL_TILE
 #undef GEMM_DFRAGS
 #undef GEMM_MAINLOOP
-  if (do_cs && wj == 0) {
+  if constexpr (NBUF > 0) {
+    if (do_cs) {
 #pragma unroll
-    for (int ti = 0; ti < TI; ti++) {
-      const float t = cs[ti] + __shfl_xor(cs[ti], 32, 64);  // the two halves of each row's reduction values
-      const int i = i0 + wi * WTI + ti * 32 + (lane & 31);
-      if (lane < 32 && i < g.M) g.colsum[(int64_t)split * g.colsum_stride + i] = t;
+      for (int ti = 0; ti < TI; ti++) {
+        if (ti % WJ != wj) continue;
+        const float t = cs[ti] + __shfl_xor(cs[ti], 32, 64);  // the two halves of each row's reduction values
+        const int i = i0 + wi * WTI + ti * 32 + (lane & 31);
+        if (lane < 32 && i < g.M) g.colsum[(int64_t)split * g.colsum_stride + i] = t;
+      }
+    }
+  } else if constexpr (HAS_CS) {
+    if (do_cs) {
+      // thread (m, c) summed rows c*VE .. c*VE+VE-1 over the reduction rows m,
+      // m + NT/CPR, ... of every step; the groups m are added in order
+      constexpr int CPRA = OA::CPR, GROUPS = NT / CPRA;
+      static_assert(GROUPS * BM * 4 <= (int)sizeof(smem), "row-sum staging fits the LDS block");
+      float* red = reinterpret_cast<float*>(smem);
+      __syncthreads();  // every wave has read its last fragments
+#pragma unroll
+      for (int e = 0; e < OA::VE; e++) red[(tid / CPRA) * BM + (tid % CPRA) * OA::VE + e] = rs[e];
+      __syncthreads();
+      for (int r = tid; r < BM; r += NT) {
+        float t = 0.f;
+#pragma unroll
+        for (int m = 0; m < GROUPS; m++) t += red[m * BM + r];
+        if (i0 + r < g.M) g.colsum[(int64_t)split * g.colsum_stride + i0 + r] = t;
+      }
     }
   }
   gemm_epilogue<T, BM, BN, WI, WJ, EPI, FP8, false>(g, acc, smem, i0, j0, split, tid, lane, wi, wj);
@@ -784,9 +833,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_persist_kernel(GemmArgs g) 
   __shared__ __attribute__((aligned(16))) char smem[OPER_BYTES > STAGE_BYTES ? OPER_BYTES : STAGE_BYTES];
   T (*sA)[OA::ELEMS] = reinterpret_cast<T (*)[OA::ELEMS]>(smem);
   T (*sB)[OB::ELEMS] = reinterpret_cast<T (*)[OB::ELEMS]>(smem + 2 * OA::ELEMS * sizeof(T));
-  constexpr bool PIPE = true, CSV = false, ILV = NSUB >= 4;
-  float cs[TI];  // (no bias-gradient sums here; named for the shared compute macros)
-  (void)cs;
+  constexpr bool PIPE = true, ILV = NSUB >= 4;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wi = wave / WJ, wj = wave % WJ;
@@ -841,10 +888,10 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_persist_kernel(GemmArgs g) 
       a0.load((kt + 2) * BK);
       b0.load((kt + 2) * BK);
       if constexpr (ILV) {
-        GEMM_COMPUTE_ST(sA[0], sB[0], CSV, PIPE,
+        GEMM_COMPUTE_ST(sA[0], sB[0], PIPE,
                         (a1.template store_part<NSUB>(sA[1], tid, ks), b1.template store_part<NSUB>(sB[1], tid, ks)))
       } else {
-        GEMM_COMPUTE(sA[0], sB[0], CSV, PIPE)
+        GEMM_COMPUTE(sA[0], sB[0], PIPE)
         a1.store(sA[1], tid);
         b1.store(sB[1], tid);
       }
@@ -852,10 +899,10 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_persist_kernel(GemmArgs g) 
       a1.load((kt + 3) * BK);
       b1.load((kt + 3) * BK);
       if constexpr (ILV) {
-        GEMM_COMPUTE_ST(sA[1], sB[1], CSV, PIPE,
+        GEMM_COMPUTE_ST(sA[1], sB[1], PIPE,
                         (a0.template store_part<NSUB>(sA[0], tid, ks), b0.template store_part<NSUB>(sB[0], tid, ks)))
       } else {
-        GEMM_COMPUTE(sA[1], sB[1], CSV, PIPE)
+        GEMM_COMPUTE(sA[1], sB[1], PIPE)
         a0.store(sA[0], tid);
         b0.store(sB[0], tid);
       }
@@ -868,10 +915,10 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_persist_kernel(GemmArgs g) 
     a0.load(0);
     b0.load(0);
     if constexpr (ILV) {
-      GEMM_COMPUTE_ST(sA[0], sB[0], CSV, PIPE,
+      GEMM_COMPUTE_ST(sA[0], sB[0], PIPE,
                       (a1.template store_part<NSUB>(sA[1], tid, ks), b1.template store_part<NSUB>(sB[1], tid, ks)))
     } else {
-      GEMM_COMPUTE(sA[0], sB[0], CSV, PIPE)
+      GEMM_COMPUTE(sA[0], sB[0], PIPE)
       a1.store(sA[1], tid);
       b1.store(sB[1], tid);
     }
@@ -880,7 +927,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_persist_kernel(GemmArgs g) 
     b1.init(Bm, g.ldb, j0n, g.N, tid);
     a1.load(BK);
     b1.load(BK);
-    GEMM_COMPUTE(sA[1], sB[1], CSV, PIPE)
+    GEMM_COMPUTE(sA[1], sB[1], PIPE)
     gemm_epilogue<T, BM, BN, WI, WJ, EPI, false, true>(g, acc, smem, i0, j0, 0, tid, lane, wi, wj);
     if (!has_next) break;
     __syncthreads();  // every wave has read its last staged chunk
