@@ -505,7 +505,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const f32x16 (&
 // TIn: operand type (T, or FP8 E4M3 with T = bf16 outputs: reduction-
 // contiguous operands, register staging, acc(i, j) scaled by scale_a[i] *
 // scale_b[j] before the epilogue).
-template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI, int NBUF, typename TIn>
+template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI, int NBUF, typename TIn,
+          int GM = 4>
 __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split) {
   constexpr int NT = WI * WJ * 64;
   constexpr int WTI = BM / WI, WTJ = BN / WJ;
@@ -535,7 +536,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split
   const int wi = wave / WJ, wj = wave % WJ;
   const int nbi = (g.M + BM - 1) / BM, nbj = (g.N + BN - 1) / BN;
   // Grouped tile order: GM consecutive row-tiles sweep the columns together.
-  constexpr int GM = 4;
   const int group = tile / (GM * nbj);
   const int first_i = group * GM;
   const int gsize = min(nbi - first_i, GM);
@@ -795,7 +795,11 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_kernel(GemmArgs g) {
 // Several independent products of one shape class in one launch (the weight
 // gradients of a layer): problem p owns the logical blocks [block0[p],
 // block0[p+1]), split-major inside it as in gemm_kernel; the blocks are
-// renumbered so each XCD takes one contiguous range of logical blocks.
+// renumbered so each XCD takes one contiguous range of logical blocks.  Tiles
+// go in groups of three row tiles: a 768-wide product's split is then whole
+// groups of 3 x 3 tiles, so where an XCD's range ends inside a split it cuts
+// between row tiles and the two XCDs share only the column operand's panels
+// (the caller orders the problems so those cuts are few).
 template <typename T, int BM, int BN, int BK, int WI, int WJ, int AT, int BT, int EPI>
 __global__ void __launch_bounds__(WI * WJ * 64) gemm_group_kernel(GemmGroup gg) {
   const int logical = xcd_remap_any(blockIdx.x, gg.block0[gg.count]);
@@ -806,7 +810,7 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_group_kernel(GemmGroup gg) 
   const GemmArgs& g = gg.p[p];
   const int nt = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   const int local = logical - gg.block0[p];
-  gemm_body<T, BM, BN, BK, WI, WJ, AT, BT, EPI, 0, T>(g, local % nt, local / nt);
+  gemm_body<T, BM, BN, BK, WI, WJ, AT, BT, EPI, 0, T, 3>(g, local % nt, local / nt);
 }
 
 // Persistent variant for forward and input-gradient products with several

@@ -140,7 +140,8 @@ struct Plan {
   // when the weight gradients of a layer run as one grouped launch)
   int64_t dres_lp2 = -1;
   // grouped weight gradients (bf16): the split-K partials and column-sum
-  // partials of a layer's four products, and their split counts
+  // partials of a layer's four products (qkv, fc, proj, fcproj), and their
+  // split counts
   int64_t gpart = -1, gcs = -1;
   int gsplit[4] = {1, 1, 1, 1};
   int64_t normpart;
@@ -222,11 +223,13 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
   if (prec == GPT2_BF16) {
     const int gt = gemm_group_tiles(3 * Ci, Ci) + gemm_group_tiles(Ci, Ci) + gemm_group_tiles(4 * Ci, Ci) +
                    gemm_group_tiles(Ci, 4 * Ci);
+    // the grouped launch's problem order: qkv, fc, proj, fcproj
+    const int64_t gsz[4] = {3 * C * C, 4 * C * C, C * C, 4 * C * C}, gout[4] = {3 * C, 4 * C, C, C};
     int64_t wp = 0, cp = 0;
     for (int k = 0; k < 4; k++) {
-      P.gsplit[k] = gemm_group_split_hint((int)wout[k], (int)(wsz[k] / wout[k]), Mi, gt);
-      if (P.gsplit[k] > 1) wp += (int64_t)P.gsplit[k] * wsz[k];
-      cp += (int64_t)P.gsplit[k] * wout[k];
+      P.gsplit[k] = gemm_group_split_hint((int)gout[k], (int)(gsz[k] / gout[k]), Mi, gt);
+      if (P.gsplit[k] > 1) wp += (int64_t)P.gsplit[k] * gsz[k];
+      cp += (int64_t)P.gsplit[k] * gout[k];
     }
     P.gpart = take(4 * std::max<int64_t>(wp, 1));
     P.gcs = take(4 * cp);
@@ -1039,9 +1042,12 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
         SideSection side(h);
         if ((rc = side.open())) return rc;
         rc = flush_reductions(h);  // the layer above's partial sums (and this layer's LayerNorm 2's)
+        // (order: at 124M each XCD's range of the launch then holds whole
+        // splits of the qkv product and cuts the others between row or
+        // column tiles only)
         const WGrad w[4] = {{dqkv, h->w<void>(P.h1[l]), 3 * C, C, h->G32(T_QKVW, l), h->G32(T_QKVB, l)},
-                            {ln2_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l)},
                             {du, h->w<void>(P.h2[l]), 4 * C, C, h->G32(T_FCW, l), h->G32(T_FCB, l)},
+                            {ln2_op, h->w<void>(P.atty[l]), C, C, h->G32(T_PROJW, l), h->G32(T_PROJB, l)},
                             {dres_op_l, h->w<void>(P.g[l]), C, 4 * C, h->G32(T_FCPW, l), h->G32(T_FCPB, l)}};
         if (!rc) rc = weight_grad_group(h, w, acc);
         if (rc || (rc = side.close_event(h->ev_layer[l & 1]))) return rc;
