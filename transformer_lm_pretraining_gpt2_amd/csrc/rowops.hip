@@ -486,20 +486,28 @@ __global__ void __launch_bounds__(CE_T) ce_kernel(T* __restrict__ logits, const 
   const int y = min(max(tgt[row], 0), V - 1);  // out-of-range targets were flagged by the embedding pass
   if (tid == 0) zt = to_f<T>(z[y]);
   constexpr float L2E = 1.4426950408889634f;
-  // load this thread's vectors (held as loaded); columns >= V count as -inf
+  // load this thread's vectors (held as loaded); columns >= V count as -inf.
+  // Only vectors k >= kfull can reach past V (a block-wide bound): the others
+  // take a copy of each pass without the column test (a scalar branch per k).
   F zv[NV];
   float mt = -INFINITY;
-  auto val = [&](int k, int q) {
+  const int kfull = V / (CE_T * 8);
+  auto val = [&](int k, int q, auto check) {
     const int vi = tid + k * CE_T;
-    return vi * 8 + q < V ? to_f<T>(zv[k][q]) : -INFINITY;
+    return !decltype(check)::value || vi * 8 + q < V ? to_f<T>(zv[k][q]) : -INFINITY;
   };
 #pragma unroll
   for (int k = 0; k < NV; k++) {
     const int vi = tid + k * CE_T;
     if (vi < nvec) {
       zv[k] = __builtin_nontemporal_load(reinterpret_cast<const F*>(z + vi * 8));
+      if (k < kfull) {
 #pragma unroll
-      for (int q = 0; q < 8; q++) mt = fmaxf(mt, val(k, q));
+        for (int q = 0; q < 8; q++) mt = fmaxf(mt, val(k, q, std::false_type{}));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; q++) mt = fmaxf(mt, val(k, q, std::true_type{}));
+      }
     }
   }
   // sum of e = exp(z - m_t) (a thread without real columns keeps m_t = -inf, st = 0)
@@ -509,8 +517,13 @@ __global__ void __launch_bounds__(CE_T) ce_kernel(T* __restrict__ logits, const 
   for (int k = 0; k < NV; k++) {
     const int vi = tid + k * CE_T;
     if (vi < nvec) {
+      if (k < kfull) {
 #pragma unroll
-      for (int q = 0; q < 8; q++) st += __builtin_amdgcn_exp2f(fmaf(val(k, q), L2E, -mtl));
+        for (int q = 0; q < 8; q++) st += __builtin_amdgcn_exp2f(fmaf(val(k, q, std::false_type{}), L2E, -mtl));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; q++) st += __builtin_amdgcn_exp2f(fmaf(val(k, q, std::true_type{}), L2E, -mtl));
+      }
     }
   }
   // combine (m_t, st) over the block: M = max m_t, S = sum st * exp(m_t - M)
@@ -531,19 +544,28 @@ __global__ void __launch_bounds__(CE_T) ce_kernel(T* __restrict__ logits, const 
   if (tid == 0) row_loss[row] = lse - zt;
   if (!write_grad) return;
   const float f = st > 0.f ? __builtin_amdgcn_exp2f((mt - lse) * L2E) * dscale : 0.f;
+  // the target's column gets softmax - 1: its thread rewrites that one value
+  // after the vector stores (the same thread, so in program order)
+  const bool owns_y = (y / 8) % CE_T == tid;
+  auto grad = [&](int k, auto check) {
+    const int vi = tid + k * CE_T;
+    F o;
+#pragma unroll
+    for (int q = 0; q < 8; q++) o[q] = from_f<T>(__builtin_amdgcn_exp2f(fmaf(val(k, q, check), L2E, -mtl)) * f);
+    __builtin_nontemporal_store(o, reinterpret_cast<F*>(z + vi * 8));
+  };
 #pragma unroll
   for (int k = 0; k < NV; k++) {
-    const int vi = tid + k * CE_T;
-    if (vi < nvec) {
-      F o;
-#pragma unroll
-      for (int q = 0; q < 8; q++) {
-        float g = __builtin_amdgcn_exp2f(fmaf(val(k, q), L2E, -mtl)) * f;
-        if (vi * 8 + q == y) g -= dscale;
-        o[q] = from_f<T>(g);
-      }
-      __builtin_nontemporal_store(o, reinterpret_cast<F*>(z + vi * 8));
+    if (tid + k * CE_T < nvec) {
+      if (k < kfull) grad(k, std::false_type{});
+      else grad(k, std::true_type{});
     }
+  }
+  if (owns_y) {
+    // the same exponential as in its vector (zt is that logit), less 1, in one
+    // rounding (a fused multiply-add)
+    const float e = __builtin_amdgcn_exp2f(fmaf(zt, L2E, -mtl));
+    z[y] = from_f<T>(fmaf(e, f, -dscale));
   }
 }
 
