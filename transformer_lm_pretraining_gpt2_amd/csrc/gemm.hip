@@ -167,11 +167,6 @@ __device__ __forceinline__ float frag_sum(bf16x8 f, float acc) {
   for (int e = 0; e < 8; e += 2) acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{f[e], f[e + 1]}, one, acc, false);
   return acc;
 }
-__device__ __forceinline__ float frag_sum(f32x8 f, float acc) {
-#pragma unroll
-  for (int e = 0; e < 8; e++) acc += f[e];
-  return acc;
-}
 
 // Direct-to-LDS operand tile (bf16): buffer_load ... lds moves each lane's 16
 // bytes from global memory straight into LDS, with no staging registers.  One
