@@ -1041,14 +1041,20 @@ hipError_t launch_tiled(hipStream_t st, const GemmArgs& g, TileKind k) {
     if constexpr (AT == 0 && BT == 0) {
       if (k == TILE_D256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI, 64, 2>(st, g);
     }
+    // the GELU' epilogue on two reduction-contiguous operands: the direct-to-LDS
+    // 256x256 tile, the 256x192 tile and the 128x128 tile only (the register
+    // path 256x256 tile spills with it; gemm() maps those choices away)
+    constexpr bool no256 = EPI == EPI_GELU_BWD && AT == 0 && BT == 0;
     if constexpr (AT == 0) {
       if (k == TILE_192_W8) return launch<T, 256, 192, 4, 2, AT, BT, EPI, 64>(st, g);
-      if constexpr (EPI != EPI_F32) {
+      if constexpr (EPI != EPI_F32 && !no256) {
         if (k == TILE_P192_W8) return launch_persist<T, 256, 192, 4, 2, BT, EPI, 64>(st, g);
         if (k == TILE_P256_W8) return launch_persist<T, 256, 256, 2, 4, BT, EPI, 64>(st, g);
       }
     }
-    if (k == TILE_256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI, 64>(st, g);
+    if constexpr (!no256) {
+      if (k == TILE_256_W8) return launch<T, 256, 256, 2, 4, AT, BT, EPI, 64>(st, g);
+    }
     if constexpr (AT == 1) {
       if (k == TILE_256x192_K32) return launch<T, 256, 192, 2, 2, AT, BT, EPI, 32>(st, g);
       if (k == TILE_256_W8_K32) return launch<T, 256, 256, 2, 4, AT, BT, EPI, 32>(st, g);
@@ -1066,6 +1072,7 @@ hipError_t dispatch(hipStream_t st, int a_t, int b_t, int epi, const GemmArgs& g
     if (epi == EPI_STORE) return launch_tiled<T, 0, 0, EPI_STORE>(st, g, k);
     if (epi == EPI_GELU) return launch_tiled<T, 0, 0, EPI_GELU>(st, g, k);
     if (epi == EPI_RESID) return launch_tiled<T, 0, 0, EPI_RESID>(st, g, k);
+    if (epi == EPI_GELU_BWD) return launch_tiled<T, 0, 0, EPI_GELU_BWD>(st, g, k);
   } else if (!a_t && b_t) {
     if (epi == EPI_STORE) return launch_tiled<T, 0, 1, EPI_STORE>(st, g, k);
     if (epi == EPI_GELU_BWD) return launch_tiled<T, 0, 1, EPI_GELU_BWD>(st, g, k);
@@ -1078,7 +1085,9 @@ hipError_t dispatch(hipStream_t st, int a_t, int b_t, int epi, const GemmArgs& g
 }  // namespace
 
 hipError_t gemm(hipStream_t st, Prec p, int a_t, int b_t, int epi, const GemmArgs& g) {
-  const TileKind k = choose_tile(p, a_t, b_t, g.M, g.N, g.K);
+  TileKind k = choose_tile(p, a_t, b_t, g.M, g.N, g.K);
+  if (epi == EPI_GELU_BWD && !a_t && !b_t)
+    k = (k == TILE_P256_W8 || k == TILE_256_W8) ? TILE_D256_W8 : k == TILE_P192_W8 ? TILE_192_W8 : k;
   return p == BF16 ? dispatch<bf16>(st, a_t, b_t, epi, g, k) : dispatch<float>(st, a_t, b_t, epi, g, k);
 }
 

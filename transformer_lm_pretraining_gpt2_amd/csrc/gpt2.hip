@@ -151,6 +151,9 @@ struct Plan {
   // like the flat parameters) with its row scales, and one FP8 activation
   // buffer with per-row scales shared by the forward's products
   int64_t w8 = -1, wsc = -1, a8 = -1, asc = -1;
+  // bf16: each layer's MLP down-projection weight transposed, [4C][C] per
+  // layer, rebuilt by every training forward for the backward's GELU' product
+  int64_t wt = -1;
   std::vector<int> split;  // split-K factor per layer weight kind (qkv, proj, fc, fcproj)
 };
 
@@ -233,6 +236,7 @@ Plan make_plan(const gpt2_config_t& c, int B, int T, int prec) {
     }
     P.gpart = take(4 * std::max<int64_t>(wp, 1));
     P.gcs = take(4 * cp);
+    P.wt = take(2 * L * 4 * C * C);
   }
   if (fp8) {
     P.w8 = take(make_layout(c).total);
@@ -441,6 +445,22 @@ GemmArgs dx_args(gpt2_t* h, const void* dY, const void* W, int N, int K, void* o
   g.C = out;
   g.ldc = K;
   return g;
+}
+
+// The MLP down-projection's input gradient times GELU'(u) of the forward:
+// du [M, 4C] = (dres [M, C] W [C, 4C]) * gelu'.  bf16 reads the transposed
+// weight copy the training forward made ([4C, C], so both operands are
+// reduction-contiguous, which selects the direct-to-LDS 256x256 tile at
+// the model widths); fp32 reads W.
+int fcproj_dx(gpt2_t* h, const void* dres, int l, void* du) {
+  const int C = h->cfg.n_embd;
+  const bool tr = h->prec == BF16;
+  GemmArgs g = tr ? fwd_args(h, dres, h->w<__bf16>(h->plan.wt) + (int64_t)l * 4 * C * C, 4 * C, C, du, nullptr)
+                  : dx_args(h, dres, h->W(T_FCPW, l), C, 4 * C, du);
+  g.aux = h->w<void>(h->plan.u[l]);
+  g.ldaux = 4 * C;
+  g.preact = h->recompute;
+  return run_gemm(h, K_GEMM_NN_GELU_BWD, 0, tr ? 0 : 1, EPI_GELU_BWD, g, "fcproj dx");
 }
 
 // Partial sums wait in a queue until the layer's backward is done; then one
@@ -819,6 +839,11 @@ static int forward_impl(gpt2_t* h, const int32_t* d_idx, const int32_t* d_target
     rc = hip_check(h, embed_sort(sst, d_idx, Mi, c.vocab_size, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva),
                                  h->w<int32_t>(P.skb), h->w<int32_t>(P.svb), h->w<int32_t>(P.seg), h->w<int32_t>(P.nseg)),
                    "embed_sort");
+    // (bf16) the transposed MLP down-projection weights the backward's GELU'
+    // product reads, from the current bf16 copy
+    if (!rc && h->prec == BF16)
+      rc = hip_check(h, transpose_bf16(sst, h->W(T_FCPW, 0), 12 * (int64_t)C * C, h->w<void>(P.wt), C, 4 * C, L),
+                     "fcproj transpose");
     if (!rc && h->overlap) rc = hip_check(h, hipEventRecord(h->ev_done[4], h->side), "sort done");
     if (rc) return rc;
   }
@@ -1008,11 +1033,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
       void* dqkv = h->w<void>((l & 1) ? P.dqkv2 : P.dqkv);
       const int64_t lp2_off = P.lp2[l & 1];
       void* ln2_op = h->w<void>(lp2_off);
-      g = dx_args(h, dres_op_l, h->W(T_FCPW, l), C, 4 * C, du);
-      g.aux = h->w<void>(P.u[l]);
-      g.ldaux = 4 * C;
-      g.preact = h->recompute;
-      if ((rc = run_gemm(h, K_GEMM_NN_GELU_BWD, 0, 1, EPI_GELU_BWD, g, "fcproj dx"))) return rc;
+      if ((rc = fcproj_dx(h, dres_op_l, l, du))) return rc;
       g = dx_args(h, du, h->W(T_FCW, l), 4 * C, C, h->w<void>(P.dh));
       if ((rc = run_gemm(h, K_GEMM_NN_STORE, 0, 1, EPI_STORE, g, "fc dx"))) return rc;
       if ((rc = ln_backward(h, h->w<void>(P.dh), h->w<float>(P.x_mid[l]), h->w<float>(P.mean2[l]),
@@ -1100,11 +1121,7 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
       if (rc || (rc = side.close(3))) return rc;
     }
     if (strict && l < L - 1 && (rc = join_side(h, 2))) return rc;  // the layer above's fc weight gradient read du
-    g = dx_args(h, dres_op, h->W(T_FCPW, l), C, 4 * C, du);
-    g.aux = h->w<void>(P.u[l]);
-    g.ldaux = 4 * C;
-    g.preact = h->recompute;
-    if ((rc = run_gemm(h, K_GEMM_NN_GELU_BWD, 0, 1, EPI_GELU_BWD, g, "fcproj dx"))) return rc;
+    if ((rc = fcproj_dx(h, dres_op, l, du))) return rc;
     // MLP up-projection
     {
       SideSection side(h);

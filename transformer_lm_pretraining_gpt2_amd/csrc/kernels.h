@@ -135,6 +135,10 @@ hipError_t adamw(hipStream_t st, float* p, const float* g, float* m, float* v, v
                  const int* skip);
 // bf16 copy of fp32 values
 hipError_t to_bf16(hipStream_t st, const float* src, void* dst, int64_t n);
+// Transposed copies of `count` bf16 matrices [rows][cols], the z-th at
+// in + z * in_stride (elements), into out[z][cols][rows] (contiguous).
+// rows and cols multiples of 64.
+hipError_t transpose_bf16(hipStream_t st, const void* in, int64_t in_stride, void* out, int rows, int cols, int count);
 // FP8 E4M3 copies of bf16 rows with one scale per row (x ~= q * scale[row]):
 // scale = max|row| / 448, q = round(x / scale).  K a multiple of 8, <= 4096.
 hipError_t quant_rows(hipStream_t st, const void* x, unsigned char* q, float* scale, int rows, int K);

@@ -758,6 +758,33 @@ __global__ void to_bf16_kernel(const float* __restrict__ src, bf16* __restrict__
     dst[i] = (bf16)src[i];
 }
 
+// One 64 x 64 tile of a bf16 matrix transposed through LDS: rows read and
+// columns written as 16-byte runs (each of the 256 threads moves two runs of
+// eight values each way).  Grid (cols/64, rows/64, matrices).
+__global__ void __launch_bounds__(256) transpose_bf16_kernel(const bf16* __restrict__ in, int64_t in_stride,
+                                                             bf16* __restrict__ out, int rows, int cols) {
+  __shared__ bf16 t[64][64 + 2];  // odd word pitch: the column reads fall in distinct banks
+  const bf16* src = in + (int64_t)blockIdx.z * in_stride;
+  bf16* dst = out + (int64_t)blockIdx.z * rows * cols;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    const int idx = threadIdx.x + 256 * k, r = idx / 8, c = (idx % 8) * 8;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(src + (int64_t)(r0 + r) * cols + c0 + c);
+#pragma unroll
+    for (int e = 0; e < 8; e++) t[r][c + e] = v[e];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    const int idx = threadIdx.x + 256 * k, c = idx / 8, r = (idx % 8) * 8;
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; e++) v[e] = t[r + e][c];
+    *reinterpret_cast<bf16x8*>(dst + (int64_t)(c0 + c) * rows + r0 + r) = v;
+  }
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -963,6 +990,13 @@ hipError_t gelu_fwd(hipStream_t st, Prec p, const void* u, void* out, int64_t n)
   else
     hipLaunchKernelGGL(gelu_fwd_kernel<float>, dim3(blocks), dim3(256), 0, st, static_cast<const float*>(u),
                        static_cast<float*>(out), n8);
+  return hipGetLastError();
+}
+
+hipError_t transpose_bf16(hipStream_t st, const void* in, int64_t in_stride, void* out, int rows, int cols, int count) {
+  if (rows <= 0 || cols <= 0 || rows % 64 != 0 || cols % 64 != 0 || count < 1 || count > 65535) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(cols / 64, rows / 64, count), dim3(256), 0, st,
+                     static_cast<const bf16*>(in), in_stride, static_cast<bf16*>(out), rows, cols);
   return hipGetLastError();
 }
 
