@@ -1193,14 +1193,16 @@ int gpt2_backward(gpt2_t* h, int micro_step, int grad_accum_steps) {
     rc = flush_reductions(h);
     if (rc || (rc = side.close(6))) return rc;
   }
-  if ((rc = join_side(h, 6))) return rc;  // everything on the second stream but the tied head
-  if ((rc = join_side(h, 5))) return rc;  // the tied head's weight gradient (second stream)
-  // embeddings: position rows and the (tied) token rows, in a fixed order
+  // embeddings: position rows and the (tied) token rows, in a fixed order,
+  // after the tied head's weight gradient (which wrote dwte first) and beside
+  // layer 0's weight gradients and reductions, which touch neither
+  if ((rc = join_side(h, 5))) return rc;
   rc = hip_check(h, embed_bwd(h->st, dres, h->w<int32_t>(P.ska), h->w<int32_t>(P.sva), h->w<int32_t>(P.seg),
                               h->w<int32_t>(P.nseg), h->G32(T_WTE), h->G32(T_WPE), h->w<float>(P.piece), h->B, h->T,
                               c.max_seq_len, C, c.vocab_size, acc),
                  "embed_bwd");
-  return rc;
+  if (rc) return rc;
+  return join_side(h, 6);  // everything else on the second stream
 }
 
 int gpt2_adamw_step(gpt2_t* h, int step, float lr, float beta1, float beta2, float eps, float weight_decay,
