@@ -1018,6 +1018,11 @@ TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
   if (a_t && b_t) return TILE_256_W8_K32;
   auto rounds = [&](int bn) { return (int64_t)((M + 255) / 256) * ((N + bn - 1) / bn) > kPersistBlocks; };
   const bool even = K % 128 == 0;  // an even number of 64-deep reduction steps
+  // an input gradient with a very long reduction (the tied head's, over the
+  // vocabulary): the 256x256 tile's main loop is faster per CU than the
+  // 256x192 one's, and the CUs a 768-wide output leaves idle go to the head's
+  // weight gradient, which runs beside it
+  if (b_t && K >= 16384 && N % 256 == 0 && mn >= 4000000) return TILE_256_W8;
   // 192-wide outputs: the model-width products, the qkv projection, and the
   // MLP's input gradient (whose GELU' epilogue spills on the 256-wide tile)
   if (N % 192 == 0 && (N <= 2304 || b_t) && mn >= 4000000)
