@@ -360,10 +360,17 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& g, const f32x16 (&
   }
   f32x8 bv[NBV];
 #pragma unroll
-  for (int k = 0; k < NBV; k++) {
-    const int j = j0 + ((tid + k * NT) % CPRW) * 8;
-    bv[k] = f32x8{};
-    if (HOIST && use_bias && j < g.N) bv[k] = ld8(g.bias + j);
+  for (int k = 0; k < NBV; k++) bv[k] = f32x8{};
+  if (HOIST && use_bias) {
+    // (a uniform branch, with its own wait: a product without a bias waits
+    // for nothing here, and the chunks below wait for no load, so the
+    // stores of one chunk never wait on those of the chunk before it)
+#pragma unroll
+    for (int k = 0; k < NBV; k++) {
+      const int j = j0 + ((tid + k * NT) % CPRW) * 8;
+      if (j < g.N) bv[k] = ld8(g.bias + j);
+    }
+    wait_vm<0>();
   }
   constexpr int PASS_UNROLL = UNROLL ? WI : 1;
 #pragma unroll PASS_UNROLL
@@ -908,9 +915,14 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_persist_kernel(GemmArgs g) 
       __syncthreads();
     }
     // the last two steps (nk-2 in buffer 0, nk-1 in registers 1); the
-    // registers 0 and then 1 take the next tile's first two steps
-    a0.init(A, g.lda, i0n, g.M, tid);
-    b0.init(Bm, g.ldb, j0n, g.N, tid);
+    // registers 0 and then 1 take the next tile's first two steps.  The
+    // next tile's load offsets are derived from an opaque copy of the thread
+    // index, so the compiler recomputes their per-thread parts here instead
+    // of keeping them live through the whole loop (where they spilled).
+    int tid_o = tid;
+    asm volatile("" : "+v"(tid_o));
+    a0.init(A, g.lda, i0n, g.M, tid_o);
+    b0.init(Bm, g.ldb, j0n, g.N, tid_o);
     a0.load(0);
     b0.load(0);
     if constexpr (ILV) {
@@ -922,8 +934,8 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_persist_kernel(GemmArgs g) 
       b1.store(sB[1], tid);
     }
     __syncthreads();
-    a1.init(A, g.lda, i0n, g.M, tid);
-    b1.init(Bm, g.ldb, j0n, g.N, tid);
+    a1.init(A, g.lda, i0n, g.M, tid_o);
+    b1.init(Bm, g.ldb, j0n, g.N, tid_o);
     a1.load(BK);
     b1.load(BK);
     GEMM_COMPUTE(sA[1], sB[1], PIPE)
