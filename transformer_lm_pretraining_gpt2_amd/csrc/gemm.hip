@@ -301,6 +301,26 @@ __device__ __forceinline__ void dtl_schedule() {
   __builtin_amdgcn_sched_group_barrier(0x008, NM - (NR + 1) / 2, 0);  // the remaining MFMAs
 }
 
+// Register-path substep order (with the next substep's fragment reads issued
+// in this one): each of the first MFMAs is followed by two of those LDS
+// reads, then by one of the next tile's LDS stores, the rest of the MFMAs
+// last, so the reads' latency hides behind the matrix core.
+template <int NM, int NR, int NW>
+__device__ __forceinline__ void reg_schedule() {
+  constexpr int GR = (NR + 1) / 2, GW = NW, REST = NM - GR - GW > 0 ? NM - GR - GW : 0;
+#pragma unroll
+  for (int r = 0; r < GR; r++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+  }
+#pragma unroll
+  for (int w = 0; w < GW; w++) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);
+}
+
 // Which instantiations can produce the bias gradient: weight-gradient products
 // (strided A, fp32 output) on 4-wave tiles.  The 8-wave tile serves only the
 // bias-free tied output layer; a second copy of its main loop would not fit
@@ -572,6 +592,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split
   // other buffer, which the barrier after the tile protects); with two
   // substeps the spread costs more than it hides.
   constexpr bool ILV = NSUB >= 4;
+  constexpr bool SCH_ON = true;
+  constexpr int SCH_READS = TI * (AT ? 2 : 1) + TJ * (BT ? 2 : 1);
+  constexpr int SCH_WRITES = ILV ? (OA::PER + NSUB - 1) / NSUB + (OB::PER + NSUB - 1) / NSUB : 0;
   constexpr bool HAS_CS = gemm_has_colsum(AT, EPI, WI * WJ);
 #define GEMM_FRAGS(AS, BS, KS, FA, FB)                                                            \
   _Pragma("unroll") for (int ti = 0; ti < TI; ti++) FA[ti] = OA::frag(AS, wi * WTI + ti * 32, KS, lane); \
@@ -592,6 +615,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& g, int tile, int split
       }                                                                                           \
       _Pragma("unroll") for (int ti = 0; ti < TI; ti++)                                           \
         _Pragma("unroll") for (int tj = 0; tj < TJ; tj++) mma16(acc[ti][tj], fb[cur][tj], fa[cur][ti]); \
+      if constexpr (PP && SCH_ON && sizeof(T) == 2) reg_schedule<TI * TJ, SCH_READS, SCH_WRITES>();          \
     }                                                                                             \
   }
 
@@ -840,6 +864,9 @@ __global__ void __launch_bounds__(WI * WJ * 64) gemm_persist_kernel(GemmArgs g) 
   T (*sA)[OA::ELEMS] = reinterpret_cast<T (*)[OA::ELEMS]>(smem);
   T (*sB)[OB::ELEMS] = reinterpret_cast<T (*)[OB::ELEMS]>(smem + 2 * OA::ELEMS * sizeof(T));
   constexpr bool PIPE = true, ILV = NSUB >= 4;
+  constexpr bool SCH_ON = false;  // (the ordering made this kernel spill)
+  constexpr int SCH_READS = TI + TJ * (BT ? 2 : 1);
+  constexpr int SCH_WRITES = ILV ? (OA::PER + NSUB - 1) / NSUB + (OB::PER + NSUB - 1) / NSUB : 0;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int wi = wave / WJ, wj = wave % WJ;
