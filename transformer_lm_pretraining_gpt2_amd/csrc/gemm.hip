@@ -1062,8 +1062,9 @@ TileKind choose_tile(Prec p, int a_t, int b_t, int M, int N, int K) {
   // 256x192 one's, and the CUs a 768-wide output leaves idle go to the head's
   // weight gradient, which runs beside it
   if (b_t && K >= 16384 && N % 256 == 0 && mn >= 4000000) return TILE_256_W8;
-  // 192-wide outputs: the model-width products, the qkv projection, and the
-  // MLP's input gradient (whose GELU' epilogue spills on the 256-wide tile)
+  // 192-wide outputs: the model-width products and the qkv projection (and
+  // any product with a strided second operand whose width is a multiple of
+  // 192: on the 256-wide register-path tile the GELU' epilogue spills)
   if (N % 192 == 0 && (N <= 2304 || b_t) && mn >= 4000000)
     return !a_t && !b_t && even && rounds(192) ? TILE_P192_W8 : TILE_192_W8;
   if (K >= 2048 || mn >= 40000000) {
