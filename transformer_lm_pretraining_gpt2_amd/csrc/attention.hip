@@ -233,6 +233,18 @@ __global__ void __launch_bounds__(NW * 64, 3) attn_fwd_kernel(const T* __restric
   if (lg == 0) lse[((int64_t)b * NH + h) * T_ + q] = (m + log2f(l)) * LN2;
 }
 
+// x as the sum of three bf16 values (x = h + m + l to about 2^-24 relative):
+// each remainder is exact in fp32, so the split loses only the last rounding.
+__device__ __forceinline__ void split3_bf16(float x, bf16x8& v, int at) {
+  const bf16 h = (bf16)x;
+  const float r = x - (float)h;
+  const bf16 m = (bf16)r;
+  v[at] = h;
+  v[at + 1] = m;
+  v[at + 2] = (bf16)(r - (float)m);
+  v[at + 3] = (bf16)0.f;
+}
+
 // ------------------------------------------------------------------------
 // dQ.  grid (NH*B, ceil(T/128)), heavy blocks first.  Per query column (one per lane):
 // D = rowsum(dO * O) (stored for the dK/dV kernel, which runs after this one),
@@ -281,6 +293,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
     lse2 = lse[((int64_t)b * NH + h) * T_ + q] * LOG2E;
     if (lg == 0) dsum[((int64_t)b * NH + h) * T_ + q] = dq_d;
   }
+
   f32x16 dq[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; dt++) dq[dt] = f32x16{};
@@ -360,19 +373,30 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
 // P = exp(S - LSE), dV += dO^T P, dP = dO V^T, dS = P (dP - D), dK += scale Q^T dS.
 // Per query tile: Q and dO rows (their transposes come from transposing
 // reads), and the tile's LSE and D values.
+//
+// bf16: the per-query terms enter through the matrix core.  S and dP are
+// laid out query x key, so LSE and D vary along the slots of each lane's
+// accumulator, and reading them per element would cost as many LDS bytes as
+// the S operand.  Instead each query row of the tile carries eight bf16
+// values [-LSE*sqrt(hd) as three terms, 0, -D as three terms, 0]: one more
+// MFMA per accumulator, against a ones fragment that picks the first or the
+// second triple, starts S at S - LSE*sqrt(hd) (so P = exp2(S * log2(e) /
+// sqrt(hd))) and dP at dP - D.
 // ------------------------------------------------------------------------
 template <typename T, int HD>
 __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restrict__ qkv, const T* __restrict__ dout,
                                                            const float* __restrict__ lse, const float* __restrict__ dsum,
                                                            T* __restrict__ dqkv, int T_, int NH, float sl2,
-                                                           float scale) {
+                                                           float scale, float rs) {
   typedef RowTile<T, HD> RT;
   constexpr int LD = RT::LD, ND = HD / 16, NDT = HD / 32;
   typedef typename Frag<T>::type F;
   typedef typename Quad<T>::type Q;
+  constexpr bool AUG = sizeof(T) == 2;  // per-query terms through the matrix core (bf16)
   __shared__ __attribute__((aligned(16))) T Qs[2][KT * LD];
   __shared__ __attribute__((aligned(16))) T Ds[2][KT * LD];
-  __shared__ float Ls[2][KT], Dd[2][KT];
+  __shared__ float Ls[AUG ? 1 : 2][AUG ? 1 : KT], Dd[AUG ? 1 : 2][AUG ? 1 : KT];
+  __shared__ __attribute__((aligned(16))) bf16 Aug[AUG ? 2 : 1][AUG ? KT * 8 : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id(), lr = lane & 31, lg = lane >> 5;
   const int kblk = blockIdx.y;  // early key blocks see the most queries: they dispatch first
@@ -402,6 +426,27 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
   }
   const float* lrow = lse + ((int64_t)b * NH + h) * T_;
   const float* drow = dsum + ((int64_t)b * NH + h) * T_;
+  // ones fragments (key side) that pick the LSE triple or the D triple of a
+  // query's eight augmentation values; lanes of the upper group add zeros
+  F onesL, onesD;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    onesL[e] = from_f<T>(lg == 0 && e < 3 ? 1.f : 0.f);
+    onesD[e] = from_f<T>(lg == 0 && e >= 4 && e < 7 ? 1.f : 0.f);
+  }
+  // a query's values as staged: LSE in log2 units (fp32), or the bf16
+  // augmentation row [-LSE*sqrt(hd) x3, 0, -D x3, 0]
+  auto stage_rowvals = [&](int buf, float l_nat, float d) {
+    if constexpr (AUG) {
+      bf16x8 a;
+      split3_bf16(-l_nat * rs, a, 0);
+      split3_bf16(-d, a, 4);
+      *reinterpret_cast<bf16x8*>(&Aug[buf][tid * 8]) = a;
+    } else {
+      Ls[buf][tid] = l_nat * LOG2E;
+      Dd[buf][tid] = d;
+    }
+  };
 
   const int qt_begin = (kblk * NW * WQ / KT) * KT;
   const int ntiles = (T_ - qt_begin) / KT;
@@ -410,15 +455,12 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
   qt.load(qbase + (int64_t)qt_begin * S3, S3, tid);
   ot.load(obase + (int64_t)qt_begin * C, C, tid);
   if (ldl) {
-    sl = lrow[qt_begin + tid] * LOG2E;
+    sl = lrow[qt_begin + tid];
     sd = drow[qt_begin + tid];
   }
   qt.store(Qs[0], tid);
   ot.store(Ds[0], tid);
-  if (ldl) {
-    Ls[0][tid] = sl;
-    Dd[0][tid] = sd;
-  }
+  if (ldl) stage_rowvals(0, sl, sd);
   __syncthreads();
   // One 64-query tile: prefetch the next tile, compute, stage the prefetch.
   // Only the first two tiles of a block can straddle one of its waves' keys,
@@ -432,7 +474,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
       qt.load(qbase + (int64_t)(qt0 + KT) * S3, S3, tid);
       ot.load(obase + (int64_t)(qt0 + KT) * C, C, tid);
       if (ldl) {
-        sl = lrow[qt0 + KT + tid] * LOG2E;
+        sl = lrow[qt0 + KT + tid];
         sd = drow[qt0 + KT + tid];
       }
     }
@@ -446,6 +488,11 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
       for (int c2 = 0; c2 < 2; c2++) {
         s[c2] = f32x16{};
         dp[c2] = f32x16{};
+        if constexpr (AUG) {
+          const F av = *reinterpret_cast<const F*>(&Aug[cur][(c2 * 32 + lr) * 8]);
+          mma16(s[c2], av, onesL);
+          mma16(dp[c2], av, onesD);
+        }
 #pragma unroll
         for (int ds = 0; ds < ND; ds++) {
           mma16(s[c2], ld8(Qs[cur] + (c2 * 32 + lr) * LD + ds * 16 + 8 * lg), kf[ds]);
@@ -457,9 +504,17 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int ql = c2 * 32 + 8 * (r / 4) + 4 * lg + (r % 4);
-          s[c2][r] = fast_exp2(fmaf(s[c2][r], sl2, -Ls[cur][ql]));
+          if constexpr (AUG) {
+            s[c2][r] = fast_exp2(s[c2][r] * sl2);
+          } else {
+            s[c2][r] = fast_exp2(fmaf(s[c2][r], sl2, -Ls[cur][ql]));
+          }
           if (MASK && c2 * 32 + 8 * (r / 4) + (r % 4) < lim) s[c2][r] = 0.f;
-          dp[c2][r] = s[c2][r] * (dp[c2][r] - Dd[cur][ql]);
+          if constexpr (AUG) {
+            dp[c2][r] = s[c2][r] * dp[c2][r];
+          } else {
+            dp[c2][r] = s[c2][r] * (dp[c2][r] - Dd[cur][ql]);
+          }
         }
 #pragma unroll
         for (int h2 = 0; h2 < 2; h2++) {
@@ -477,10 +532,7 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dkv_kernel(const T* __restric
     if (more) {
       qt.store(Qs[cur ^ 1], tid);
       ot.store(Ds[cur ^ 1], tid);
-      if (ldl) {
-        Ls[cur ^ 1][tid] = sl;
-        Dd[cur ^ 1][tid] = sd;
-      }
+      if (ldl) stage_rowvals(cur ^ 1, sl, sd);
     }
     __syncthreads();
   };
@@ -535,9 +587,9 @@ hipError_t dkv_t(hipStream_t st, const void* qkv, const void* dout, const float*
   // blockIdx.x (dispatched fastest) walks the heads, blockIdx.y the row
   // blocks from the most work to the least, so the long blocks start first
   dim3 grid(NH * B, (T_ + NW * WQ - 1) / (NW * WQ));
-  const float scale = 1.f / sqrtf((float)HD), sl2 = LOG2E * scale;
+  const float rs = sqrtf((float)HD), scale = 1.f / rs, sl2 = LOG2E * scale;
   hipLaunchKernelGGL((attn_dkv_kernel<T, HD>), grid, dim3(NW * 64), 0, st, static_cast<const T*>(qkv),
-                     static_cast<const T*>(dout), lse, dsum, static_cast<T*>(dqkv), T_, NH, sl2, scale);
+                     static_cast<const T*>(dout), lse, dsum, static_cast<T*>(dqkv), T_, NH, sl2, scale, rs);
   return hipGetLastError();
 }
 
