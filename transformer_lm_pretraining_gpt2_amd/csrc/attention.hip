@@ -293,7 +293,6 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_dq_kernel(const T* __restrict
     lse2 = lse[((int64_t)b * NH + h) * T_ + q] * LOG2E;
     if (lg == 0) dsum[((int64_t)b * NH + h) * T_ + q] = dq_d;
   }
-
   f32x16 dq[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; dt++) dq[dt] = f32x16{};
