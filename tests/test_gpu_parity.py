@@ -13,7 +13,7 @@ import math
 import numpy as np
 import pytest
 
-from gpu_common import batches, compare, gpu_step, oracle_step
+from gpu_common import batches, compare, gpu_step, oracle_step, rel_l2, tensor_views
 from oracle import oracle
 from transformer_lm_pretraining_gpt2_amd import binding, synth
 from transformer_lm_pretraining_gpt2_amd.config import CONFIGS, GPT2Config
@@ -364,3 +364,33 @@ def test_recompute_eval_equals_forward():
     s.forward(d_ids, d_tgt, lf)
     assert s.sync_status() == 0
     assert le.item() == lf.item()
+
+
+# head size 64 (the benchmark's), two heads
+SHARP = GPT2Config(vocab_size=509, padded_vocab_size=512, n_layer=2, n_head=2, n_embd=128, max_seq_len=256)
+
+
+def test_sharpened_attention_bf16():
+    # The q and k rows of every c_attn weight scaled by 3: attention scores of
+    # a few units, a peaked softmax and log-sum-exps far from zero.  The bf16
+    # dK/dV kernel adds -LSE*sqrt(hd) and -D to S and dP through the matrix
+    # core as three bf16 terms each; with them the step's worst per-tensor
+    # gradient error against the fp64 oracle is 2.12e-2, the same as with LSE
+    # and D read as fp32 values, while keeping only the leading bf16 term gives
+    # 2.43e-2.  The kernels are deterministic, so the bar between the two
+    # separates them.  (Scaled by 5 or more, the bf16 rounding of q and k alone
+    # puts gradients beyond the bf16 bar, whatever the kernel.)
+    B, T = 4, 256
+    lay = binding.param_layout(SHARP)
+    p0 = synth.random_params(lay, SHARP.vocab_size, seed=31, scale=0.05)
+    for e in lay:
+        if e["name"].endswith("attn.c_attn.weight"):
+            w = p0[e["offset"]:e["offset"] + e["rows"] * e["cols"]].reshape(e["rows"], e["cols"])
+            w[:2 * SHARP.n_embd] *= 3.0
+    mb = batches(SHARP, B, T, 1, seed=77)
+    g = gpu_step(SHARP, B, T, "bf16", p0, mb, lr=1e-3)
+    o = oracle_step(SHARP, p0, mb, lr=1e-3)
+    compare(SHARP, g, o, "bf16")
+    gv, ov = tensor_views(lay, g["grads"]), tensor_views(lay, o["grads"])
+    worst = max(rel_l2(gv[n], ov[n]) for n in gv if np.linalg.norm(ov[n]) > 0)
+    assert worst <= 2.25e-2, worst
